@@ -1,0 +1,300 @@
+"""Throughput of ReduceScatter + AllGather AllReduce over N virtual ranks on
+one MI355X, through the C-ABI library.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole hot path on one batch: ccl_sim_reduce_scatter followed
+by ccl_sim_all_gather (direct fused schedule) over N=8 ranks of M=2^28
+float32 each, inputs resident in HBM.  W untimed steps, then K timed steps
+between device synchronisations.  The value is effective HBM bandwidth:
+the schedule's algorithmic bytes 2(N+1)·M·4 divided by the time per step.
+
+Also reported, on the same buffers: per-kernel durations from HIP events on
+the launch stream (the roofline of the dominant kernel), the other
+schedules (ring stepwise / persistent RS+AG, direct and ring AllReduce,
+RS-only), and the CPU oracle timed on a bounded sample of the same
+workload.  Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="uniform_8x268435456_fp32")
+    p.add_argument("--secondary-iters", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle work for cpu_baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "device.hpp", "internal.hpp"):
+        with open(os.path.join(HERE, "collective_reduction_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when none were taken for this kernel and workload or the kernel source
+    has changed since."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"{kernel}:{workload}")
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def stats(ms):
+    ms = sorted(ms)
+    med = statistics.median(ms)
+    p95 = ms[min(len(ms) - 1, int(round(0.95 * (len(ms) - 1))))]
+    mean = statistics.fmean(ms)
+    cv = statistics.pstdev(ms) / mean if len(ms) > 1 and mean > 0 else 0.0
+    return {"median_ms": med, "p95_ms": p95, "mean_ms": mean, "cv": cv}
+
+
+def cpu_baseline(spec, target_s):
+    """The oracle's RS + AG timed on a bounded sample: the first qs positions
+    of every shard (so the sample keeps the rank-major structure), qs grown
+    until the oracle's own work reaches about target_s seconds."""
+    import numpy as np
+    from collective_reduction_amd import inputs as I
+    from oracle import collectives as C
+
+    n, m = spec["nranks"], spec["count"]
+    q = -(-m // n)
+    es = np.dtype(I._STORAGE[spec["dtype"]]).itemsize
+
+    def sample(qs):
+        xs = []
+        for r in range(n):
+            parts = [I.rank_buffer(spec, r, s * q, min(s * q + qs, m), workers=8) for s in range(n)]
+            xs.append(np.concatenate(parts))
+        return xs
+
+    qs = min(q, 1 << 16)
+    while True:
+        xs = sample(qs)
+        t0 = time.perf_counter()
+        shards = C.reduce_scatter(xs, "sum", spec["dtype"], qs)
+        C.all_gather(shards)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or qs >= q:
+            break
+        qs = min(q, max(qs * 2, int(qs * target_s / max(dt, 1e-3) * 1.1)))
+        del xs, shards
+    nbytes = 2 * (n + 1) * n * qs * es
+    threads = os.environ.get("OMP_NUM_THREADS")
+    return {
+        "value": nbytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {qs} positions of each of the {n} shards ({n * qs} of {m} positions per rank, "
+                  f"{n} ranks); oracle reduce_scatter + all_gather took {dt:.2f} s single-threaded NumPy",
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "omp_num_threads": threads,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: every rank here is a virtual rank in one GPU's HBM, so "
+              f"--gpus {args.gpus} is not supported (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from collective_reduction_amd import ccl_sim as cs
+    from collective_reduction_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    spec = I.spec(args.workload)
+    n, m, dtype = spec["nranks"], spec["count"], spec["dtype"]
+    q = -(-m // n)
+    if n * q != m:
+        print("the bench workload must divide into N shards", file=sys.stderr)
+        sys.exit(2)
+    tdt = {"float32": torch.float32, "bfloat16": torch.bfloat16, "int32": torch.int32, "int64": torch.int64}[dtype]
+    stream = torch.cuda.current_stream()
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device {dev_name}; workload {args.workload}: N={n} M={m} {dtype}")
+
+    # Inputs resident in HBM before timing.
+    t0 = time.time()
+    send = []
+    for r in range(n):
+        host = I.rank_buffer(spec, r, workers=16)
+        t = torch.empty(m, dtype=tdt, device="cuda")
+        if dtype == "bfloat16":
+            t.view(torch.int16).copy_(torch.from_numpy(host.view("int16")))
+        else:
+            t.copy_(torch.from_numpy(host))
+        send.append(t)
+        del host
+        log(f"rank {r} uploaded ({time.time() - t0:.1f} s)")
+    shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
+    recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
+    torch.cuda.synchronize()
+
+    bytes_rs = cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct")
+    bytes_ag = cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")
+    bytes_step = bytes_rs + bytes_ag
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        cs.ccl_sim_reduce_scatter(send, shards, m, q, op="sum", schedule="direct", stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"{args.warmup} warmup steps done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"{args.steps} timed steps done in {wall * 1e3:.1f} ms")
+
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    rs_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ag_ms = [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    value = bytes_step / (ms_per_step / 1e3) / 1e9
+
+    rs_avg, ag_avg = statistics.fmean(rs_ms), statistics.fmean(ag_ms)
+    dominant = ("rs_direct_kernel", rs_avg, bytes_rs) if rs_avg >= ag_avg else ("ag_direct_kernel", ag_avg, bytes_ag)
+    achieved = dominant[2] / (dominant[1] / 1e3) / 1e9
+    traffic = load_traffic(dominant[0], args.workload)
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": dominant[0],
+                "avg_launch_ms": dominant[1], "algorithmic_bytes_per_launch": dominant[2]}
+
+    kernels = {
+        "rs_direct_kernel": {"avg_ms": rs_avg, "bytes": bytes_rs, "gbs": bytes_rs / (rs_avg / 1e3) / 1e9,
+                             **stats(rs_ms)},
+        "ag_direct_kernel": {"avg_ms": ag_avg, "bytes": bytes_ag, "gbs": bytes_ag / (ag_avg / 1e3) / 1e9,
+                             **stats(ag_ms)},
+    }
+
+    secondary = {}
+    if not args.no_secondary:
+        secondary = run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, args.secondary_iters)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(spec, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.3f} GB/s over {cpu['seconds']:.1f} s")
+
+    out = {
+        "metric": "effective HBM GB/s (and % of peak) for RS+AG AllReduce, N=8, M=2^28 fp32",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "bfloat16": "bf16", "int32": "i32", "int64": "i64"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "nranks": n, "count": m, "op": "sum",
+                   "collective": "reduce_scatter + all_gather", "schedule": "direct",
+                   "bytes_per_step": bytes_step},
+        "frac_of_peak": value / PEAK_HBM_GBS,
+        "step_stats": stats(step_ms),
+        "elements_per_s": n * m / (ms_per_step / 1e3),
+        "roofline": roofline,
+        "kernels": kernels,
+        "secondary": secondary,
+        "cpu_baseline": cpu,
+        "device": dev_name,
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
+    """Other schedules and collectives on the same buffers, each timed with
+    HIP events over `iters` calls after one warm-up call."""
+    res = {}
+    ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
+                               for s in ("ring_stepwise", "ring_persistent")])
+
+    def timed(name, fn, nbytes):
+        try:
+            fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = [a.elapsed_time(b) for a, b in ev]
+            st = stats(ms)
+            res[name] = {"bytes": nbytes, "gbs": nbytes / (st["median_ms"] / 1e3) / 1e9,
+                         "frac_of_peak": nbytes / (st["median_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, **st}
+            log(f"{name}: {st['median_ms']:.3f} ms, {res[name]['gbs']:.0f} GB/s")
+        except Exception as e:  # a schedule this device cannot run is reported, not fatal
+            res[name] = {"error": str(e)}
+            log(f"{name}: {e}")
+
+    ab = cs.ccl_sim_algorithmic_bytes
+    for sched in ("ring_stepwise", "ring_persistent"):
+        timed(f"rs_ag_{sched}", lambda s=sched: (
+            cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
+            cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
+            ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched))
+    for sched in ("direct", "ring_stepwise", "ring_persistent"):
+        timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
+            send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
+    timed("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
+          ab("reduce_scatter", n, m, dtype, "direct"))
+    # plain copy of the same size as one rank's buffer, for scale
+    timed("copy_one_rank_torch", lambda: recv[0].copy_(send[0]), 2 * m * send[0].element_size())
+    return res
+
+
+if __name__ == "__main__":
+    main()

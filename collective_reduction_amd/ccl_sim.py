@@ -1,0 +1,288 @@
+"""ctypes binding of libccl_sim.so (declared in include/ccl_sim.h).
+
+Argument marshalling only: rank buffers given as torch tensors (or raw
+device addresses) become arrays of device pointers, torch dtypes become the
+library's dtype codes, and the current torch stream becomes the HIP stream.
+Every collective runs in the library's HIP kernels; there is no CPU path.
+A missing library raises ImportError at import.
+
+torch is imported before the library is loaded: torch ships its own HIP
+runtime under the same soname, and loading torch first makes the library
+bind to that one runtime instead of a second copy.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libccl_sim.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m collective_reduction_amd._build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError(f"two HIP runtimes are loaded: {sorted(_hip_runtimes_mapped())}")
+
+# enums (include/ccl_sim.h)
+SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, INSUFFICIENT_WORKSPACE, HIP_ERROR, CAPACITY_MISMATCH = range(6)
+DTYPES = {"int32": 0, "int64": 1, "float32": 2, "bfloat16": 3}
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
+SCHEDULES = {"direct": 0, "ring_stepwise": 1, "ring_persistent": 2}
+COLLS = {"reduce_scatter": 0, "all_gather": 1, "allreduce": 2}
+INLINE_RANKS = 64
+MAX_RANKS = 1024
+
+_TORCH_DTYPES = {torch.int32: "int32", torch.int64: "int64", torch.float32: "float32", torch.bfloat16: "bfloat16"}
+
+_c_size = ctypes.c_size_t
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+
+def _sig(name, restype, argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = argtypes
+    return fn
+
+
+_reduce_scatter = _sig("ccl_sim_reduce_scatter", ctypes.c_int,
+                       [_vpp, _vpp, ctypes.c_int, _c_size, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                        ctypes.c_void_p, _c_size, ctypes.c_void_p])
+_all_gather = _sig("ccl_sim_all_gather", ctypes.c_int,
+                   [_vpp, _vpp, ctypes.c_int, _c_size, _c_size, ctypes.c_int, ctypes.c_int,
+                    ctypes.c_void_p, _c_size, ctypes.c_void_p])
+_allreduce = _sig("ccl_sim_allreduce", ctypes.c_int,
+                  [_vpp, _vpp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, _c_size, ctypes.c_void_p])
+_pad_identity = _sig("ccl_sim_pad_identity", ctypes.c_int,
+                     [_vpp, _vpp, ctypes.c_int, _c_size, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+_workspace_size = _sig("ccl_sim_workspace_size", _c_size,
+                       [ctypes.c_int, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int])
+_algorithmic_bytes = _sig("ccl_sim_algorithmic_bytes", ctypes.c_uint64,
+                          [ctypes.c_int, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int])
+_launch_count = _sig("ccl_sim_launch_count", ctypes.c_int,
+                     [ctypes.c_int, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int])
+_ring_owner = _sig("ccl_sim_ring_owner", ctypes.c_int, [ctypes.c_int, ctypes.c_int])
+_ring_route = _sig("ccl_sim_ring_route", ctypes.c_int,
+                   [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                    ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)])
+_result_string = _sig("ccl_sim_result_string", ctypes.c_char_p, [ctypes.c_int])
+_last_error = _sig("ccl_sim_last_error", ctypes.c_char_p, [])
+_version = _sig("ccl_sim_version", ctypes.c_int, [])
+
+EXPORTED = ("ccl_sim_reduce_scatter", "ccl_sim_all_gather", "ccl_sim_allreduce", "ccl_sim_pad_identity",
+            "ccl_sim_workspace_size", "ccl_sim_algorithmic_bytes", "ccl_sim_launch_count", "ccl_sim_ring_owner",
+            "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version")
+
+
+class CclSimError(RuntimeError):
+    """A non-capacity failure reported by the library."""
+
+    def __init__(self, code, message):
+        super().__init__(message)
+        self.code = code
+
+
+def _check(code):
+    if code == SUCCESS:
+        return
+    detail = _last_error().decode()
+    what = _result_string(code).decode()
+    msg = f"{what}: {detail}" if detail else what
+    if code == CAPACITY_MISMATCH:
+        # the same exception type the PyTorch capacity check raises
+        raise TypeError(msg)
+    raise CclSimError(code, msg)
+
+
+def _enum(table, value, what):
+    if isinstance(value, int):
+        return value
+    try:
+        return table[value]
+    except KeyError:
+        raise ValueError(f"unknown {what} {value!r}; expected one of {sorted(table)}") from None
+
+
+def _dtype_code(dtype):
+    if isinstance(dtype, torch.dtype):
+        if dtype not in _TORCH_DTYPES:
+            raise ValueError(f"unsupported dtype {dtype}")
+        dtype = _TORCH_DTYPES[dtype]
+    return _enum(DTYPES, dtype, "dtype")
+
+
+def _ptr(x):
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _ptr_array(bufs):
+    arr = (ctypes.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
+    return ctypes.cast(arr, _vpp), arr
+
+
+_HAVE_GPU = None
+
+
+def _stream(stream):
+    global _HAVE_GPU
+    if stream is None:
+        if _HAVE_GPU is None:
+            _HAVE_GPU = torch.cuda.is_available()
+        # without a GPU the library rejects or fails the call itself; the
+        # null stream keeps argument validation reachable on a host
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream if _HAVE_GPU else 0)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _infer_dtype(bufs, dtype):
+    if dtype is not None:
+        return _dtype_code(dtype)
+    for b in bufs:
+        if isinstance(b, torch.Tensor):
+            return _dtype_code(b.dtype)
+    raise ValueError("dtype must be given when buffers are raw addresses")
+
+
+def _ws(workspace):
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    if isinstance(workspace, Workspace):
+        if workspace.tensor is None:
+            return ctypes.c_void_p(0), 0
+        workspace = workspace.tensor
+    if isinstance(workspace, torch.Tensor):
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    addr, nbytes = workspace
+    return ctypes.c_void_p(int(addr)), int(nbytes)
+
+
+def ccl_sim_reduce_scatter(sendbufs, recvbufs, sendcount, recvcount, op="sum", schedule="direct",
+                           workspace=None, stream=None, dtype=None):
+    """ReduceScatter over len(sendbufs) virtual ranks (rank-major shards)."""
+    n = len(sendbufs)
+    if len(recvbufs) != n:
+        raise ValueError("sendbufs and recvbufs must list the same ranks")
+    s, _ks = _ptr_array(sendbufs)
+    r, _kr = _ptr_array(recvbufs)
+    wp, wb = _ws(workspace)
+    _check(_reduce_scatter(s, r, n, sendcount, recvcount, _infer_dtype(sendbufs, dtype), _enum(OPS, op, "op"),
+                           _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+
+
+def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direct", workspace=None, stream=None,
+                       dtype=None):
+    """AllGather in source-rank order, trimmed to recvcount."""
+    n = len(sendbufs)
+    if len(recvbufs) != n:
+        raise ValueError("sendbufs and recvbufs must list the same ranks")
+    s, _ks = _ptr_array(sendbufs)
+    r, _kr = _ptr_array(recvbufs)
+    wp, wb = _ws(workspace)
+    _check(_all_gather(s, r, n, sendcount, recvcount, _infer_dtype(sendbufs, dtype),
+                       _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+
+
+def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", workspace=None, stream=None,
+                      dtype=None):
+    """AllReduce of count elements per rank (any count)."""
+    n = len(sendbufs)
+    if len(recvbufs) != n:
+        raise ValueError("sendbufs and recvbufs must list the same ranks")
+    s, _ks = _ptr_array(sendbufs)
+    r, _kr = _ptr_array(recvbufs)
+    wp, wb = _ws(workspace)
+    _check(_allreduce(s, r, n, count, _infer_dtype(sendbufs, dtype), _enum(OPS, op, "op"),
+                      _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+
+
+def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype=None):
+    """dsts[r] = srcs[r] followed by the identity of op up to padded_count."""
+    n = len(dsts)
+    if len(srcs) != n:
+        raise ValueError("srcs and dsts must list the same ranks")
+    s, _ks = _ptr_array(srcs)
+    d, _kd = _ptr_array(dsts)
+    _check(_pad_identity(s, d, n, count, padded_count, _infer_dtype(dsts, dtype), _enum(OPS, op, "op"),
+                         _stream(stream)))
+
+
+def ccl_sim_workspace_size(coll, nranks, count, dtype, schedule):
+    return _workspace_size(_enum(COLLS, coll, "coll"), nranks, count, _dtype_code(dtype),
+                           _enum(SCHEDULES, schedule, "schedule"))
+
+
+def ccl_sim_algorithmic_bytes(coll, nranks, count, dtype, schedule):
+    return _algorithmic_bytes(_enum(COLLS, coll, "coll"), nranks, count, _dtype_code(dtype),
+                              _enum(SCHEDULES, schedule, "schedule"))
+
+
+def ccl_sim_launch_count(coll, nranks, count, schedule, in_place=False):
+    return _launch_count(_enum(COLLS, coll, "coll"), nranks, count, _enum(SCHEDULES, schedule, "schedule"),
+                         int(bool(in_place)))
+
+
+def ccl_sim_ring_owner(nranks, rank):
+    return _ring_owner(nranks, rank)
+
+
+def ccl_sim_ring_route(nranks, phase, step, rank):
+    """(send_chunk, recv_chunk); phase 0 RS, 1 AG after RS, 2 stand-alone AG."""
+    s, r = ctypes.c_int(), ctypes.c_int()
+    _check(_ring_route(nranks, phase, step, rank, ctypes.byref(s), ctypes.byref(r)))
+    return s.value, r.value
+
+
+def ccl_sim_result_string(code):
+    return _result_string(code).decode()
+
+
+def ccl_sim_last_error():
+    return _last_error().decode()
+
+
+def ccl_sim_version():
+    return _version()
+
+
+class Workspace:
+    """Caller-owned device workspace sized by ccl_sim_workspace_size (a
+    torch uint8 tensor; torch allocations are at least 256-byte aligned)."""
+
+    def __init__(self, coll, nranks, count, dtype, schedule, device="cuda"):
+        nbytes = ccl_sim_workspace_size(coll, nranks, count, dtype, schedule)
+        if nbytes == ctypes.c_size_t(-1).value:
+            raise ValueError("invalid arguments for the workspace size")
+        self.nbytes = nbytes
+        self.tensor = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
+
+    @staticmethod
+    def largest(requests, device="cuda"):
+        """One workspace big enough for every (coll, nranks, count, dtype, schedule) request."""
+        w = Workspace.__new__(Workspace)
+        w.nbytes = max(ccl_sim_workspace_size(*r) for r in requests)
+        w.tensor = torch.empty(max(w.nbytes, 1), dtype=torch.uint8, device=device) if w.nbytes else None
+        return w

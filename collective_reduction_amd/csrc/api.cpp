@@ -1,0 +1,439 @@
+// C-ABI front end of libccl_sim: argument validation, planning (shard
+// length, workspace layout, in-place detection) and
+// dispatch to the kernels.  Every check runs before the first HIP call, so
+// a rejected call enqueues nothing.
+//
+// Pages cited:
+//   [DECOMP] "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
+//   [RING]   "Ring AllReduce 核心流程：梯度是怎么聚合的"
+//   [PRIMS]  "通信与互联（01）：集合通信原语与代价模型——α-β 模型与 ring all-reduce"
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "ccl_sim.h"
+#include "internal.hpp"
+
+namespace {
+
+using namespace ccl;
+
+thread_local std::string g_last_error;
+
+ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool valid_dtype(int d) { return d >= CCL_SIM_INT32 && d <= CCL_SIM_BFLOAT16; }
+bool valid_op(int o) { return o >= CCL_SIM_SUM && o <= CCL_SIM_MIN; }
+bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RING_PERSISTENT; }
+bool valid_coll(int c) { return c >= CCL_SIM_COLL_REDUCE_SCATTER && c <= CCL_SIM_COLL_ALLREDUCE; }
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// A single rank has nothing to exchange: every schedule is the direct copy.
+int effective_schedule(int nranks, int schedule) { return nranks == 1 ? CCL_SIM_DIRECT : schedule; }
+
+uint64_t shard_len(uint64_t m, int n) { return m / uint64_t(n) + (m % uint64_t(n) != 0); }
+
+// Workspace layout.  `m` is the logical per-rank length (see ccl_sim.h).
+struct Layout {
+  size_t ctrl = SIZE_MAX, send_tab = SIZE_MAX, recv_tab = SIZE_MAX, partial = SIZE_MAX;
+  size_t total = 0;
+  bool ok = true;
+};
+
+Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
+  Layout l;
+  const int sched = effective_schedule(nranks, schedule);
+  size_t off = 0;
+  if (sched == CCL_SIM_RING_PERSISTENT) {
+    l.ctrl = off;
+    off += round_up(kCtrlWords * sizeof(unsigned));
+  }
+  if (nranks > kInlineRanks) {
+    const size_t tab = round_up(size_t(nranks) * sizeof(void*));
+    l.send_tab = off;
+    l.recv_tab = off + tab;
+    off += 2 * tab;
+  }
+  if (sched != CCL_SIM_DIRECT && coll != CCL_SIM_COLL_ALL_GATHER && nranks >= 3) {
+    const uint64_t q = shard_len(m, nranks);
+    uint64_t bytes = 0;
+    if (__builtin_mul_overflow(q, uint64_t(2) * uint64_t(nranks) * accum_size(dtype), &bytes) ||
+        bytes > SIZE_MAX - off - kAlign) {
+      l.ok = false;
+      return l;
+    }
+    l.partial = off;
+    off += round_up(size_t(bytes));
+  }
+  l.total = off;
+  return l;
+}
+
+std::atomic<int> g_cus[64];
+
+hipError_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int cached = g_cus[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cus = cached;
+      return hipSuccess;
+    }
+  }
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) g_cus[dev].store(v, std::memory_order_relaxed);
+  *cus = v;
+  return hipSuccess;
+}
+
+struct Span {
+  uintptr_t lo, hi;
+  int rank;
+};
+
+// Outputs must be pairwise disjoint; an input may overlap an output only
+// when they belong to the same rank and `allowed(rank)` says the pair is the
+// in-place form.  O(N log N).
+template <class Allowed>
+bool overlap_ok(std::vector<Span> outs, const std::vector<Span>& ins, Allowed allowed, std::string* why) {
+  outs.erase(std::remove_if(outs.begin(), outs.end(), [](const Span& s) { return s.hi == s.lo; }), outs.end());
+  std::sort(outs.begin(), outs.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < outs.size(); ++i)
+    if (outs[i - 1].hi > outs[i].lo) {
+      *why = "output buffers of ranks " + std::to_string(outs[i - 1].rank) + " and " + std::to_string(outs[i].rank) +
+             " overlap";
+      return false;
+    }
+  for (const Span& in : ins) {
+    if (in.hi == in.lo) continue;
+    auto it = std::upper_bound(outs.begin(), outs.end(), in.lo, [](uintptr_t v, const Span& s) { return v < s.hi; });
+    for (; it != outs.end() && it->lo < in.hi; ++it) {
+      if (it->rank != in.rank || !allowed(in.rank)) {
+        *why = "input of rank " + std::to_string(in.rank) + " overlaps the output of rank " +
+               std::to_string(it->rank) + " outside the in-place form";
+        return false;
+      }
+    }
+  }
+  return true;
+}
+
+bool spans_clear_of(const std::vector<Span>& spans, uintptr_t lo, uintptr_t hi) {
+  for (const Span& s : spans)
+    if (s.hi > s.lo && s.lo < hi && lo < s.hi) return false;
+  return true;
+}
+
+ccl_sim_result_t check_ptrs(const void* const* ptrs, int nranks, const char* what, size_t es) {
+  if (ptrs == nullptr) return fail(CCL_SIM_INVALID_ARGUMENT, "%s array is NULL", what);
+  for (int r = 0; r < nranks; ++r) {
+    if (ptrs[r] == nullptr) return fail(CCL_SIM_INVALID_ARGUMENT, "%s[%d] is NULL", what, r);
+    if (reinterpret_cast<uintptr_t>(ptrs[r]) % es != 0)
+      return fail(CCL_SIM_INVALID_ARGUMENT, "%s[%d] is not aligned to the element size (%zu bytes)", what, r, es);
+  }
+  return CCL_SIM_SUCCESS;
+}
+
+// Shared path of the three collectives.
+ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                size_t sendcount, size_t recvcount, int dtype, int op, int schedule, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS)
+    return fail(CCL_SIM_INVALID_ARGUMENT, "nranks=%d outside [1, %d]", nranks, CCL_SIM_MAX_RANKS);
+  if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", dtype);
+  if (coll != CCL_SIM_COLL_ALL_GATHER && !valid_op(op)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid op %d", op);
+  if (!valid_sched(schedule)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid schedule %d", schedule);
+  const size_t es = elem_size(dtype);
+
+  // Counts ([DECOMP] §源码一 count rules; §Contract 实验四 capacity check).
+  uint64_t m = 0, q = 0, in_len = 0, out_len = 0;
+  if (coll == CCL_SIM_COLL_REDUCE_SCATTER) {
+    uint64_t need = 0;
+    if (__builtin_mul_overflow(uint64_t(recvcount), uint64_t(nranks), &need) || need != sendcount)
+      return fail(CCL_SIM_CAPACITY_MISMATCH,
+                  "input tensor must be the same size as output size times world size "
+                  "(sendcount=%zu, nranks=%d, recvcount=%zu)",
+                  sendcount, nranks, recvcount);
+    m = sendcount;
+    q = recvcount;
+    in_len = sendcount;
+    out_len = recvcount;
+  } else if (coll == CCL_SIM_COLL_ALL_GATHER) {
+    uint64_t have = 0;
+    if (!__builtin_mul_overflow(uint64_t(sendcount), uint64_t(nranks), &have) && recvcount > have)
+      return fail(CCL_SIM_CAPACITY_MISMATCH,
+                  "output tensor larger than input size times world size (sendcount=%zu, nranks=%d, recvcount=%zu)",
+                  sendcount, nranks, recvcount);
+    m = recvcount;
+    q = sendcount;
+    in_len = sendcount;
+    out_len = recvcount;
+  } else {
+    m = sendcount;
+    q = shard_len(m, nranks);
+    in_len = out_len = sendcount;
+  }
+  uint64_t bytes_tmp = 0;
+  if (__builtin_mul_overflow(in_len, uint64_t(es), &bytes_tmp) || __builtin_mul_overflow(out_len, uint64_t(es), &bytes_tmp))
+    return fail(CCL_SIM_INVALID_ARGUMENT, "buffer size in bytes overflows");
+  if (out_len == 0) return CCL_SIM_SUCCESS;  // nothing to compute or store
+
+  ccl_sim_result_t rc = check_ptrs(sendbufs, nranks, "sendbufs", es);
+  if (rc != CCL_SIM_SUCCESS) return rc;
+  rc = check_ptrs(const_cast<const void* const*>(recvbufs), nranks, "recvbufs", es);
+  if (rc != CCL_SIM_SUCCESS) return rc;
+
+  std::vector<Span> ins(nranks), outs(nranks);
+  for (int r = 0; r < nranks; ++r) {
+    const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
+    const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
+    ins[r] = Span{s, s + in_len * es, r};
+    outs[r] = Span{d, d + out_len * es, r};
+  }
+  auto in_place = [&](int r) -> bool {
+    const uintptr_t s = ins[r].lo, d = outs[r].lo;
+    if (coll == CCL_SIM_COLL_ALLREDUCE) return s == d;
+    if (coll == CCL_SIM_COLL_REDUCE_SCATTER) return d == s + uint64_t(r) * q * es;
+    return s == d + uint64_t(r) * q * es;
+  };
+  std::string why;
+  if (!overlap_ok(outs, ins, in_place, &why)) return fail(CCL_SIM_INVALID_ARGUMENT, "%s", why.c_str());
+
+  const int sched = effective_schedule(nranks, schedule);
+  const Layout lay = layout(coll, nranks, m, dtype, schedule);
+  if (!lay.ok) return fail(CCL_SIM_INVALID_ARGUMENT, "workspace size overflows");
+  if (lay.total > 0) {
+    if (workspace == nullptr || workspace_bytes < lay.total)
+      return fail(CCL_SIM_INSUFFICIENT_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total,
+                  workspace == nullptr ? size_t(0) : workspace_bytes, workspace == nullptr ? " (NULL)" : "");
+    const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+    if (w % kAlign != 0) return fail(CCL_SIM_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (!spans_clear_of(ins, w, w + lay.total) || !spans_clear_of(outs, w, w + lay.total))
+      return fail(CCL_SIM_INVALID_ARGUMENT, "workspace overlaps a rank buffer");
+  }
+
+  // Plan.
+  Call c;
+  c.coll = coll;
+  c.dtype = dtype;
+  c.op = op;
+  c.schedule = sched;
+  c.nranks = nranks;
+  c.q = q;
+  c.limit = (coll == CCL_SIM_COLL_REDUCE_SCATTER) ? uint64_t(nranks) * q : m;
+  c.in_place = true;
+  for (int r = 0; r < nranks && c.in_place; ++r) c.in_place = in_place(r);
+  char* ws = static_cast<char*>(workspace);
+  if (lay.partial != SIZE_MAX) c.partial = ws + lay.partial;
+  if (lay.ctrl != SIZE_MAX) c.ctrl = reinterpret_cast<unsigned*>(ws + lay.ctrl);
+  c.stream = stream;
+
+  hipError_t e = device_cus(&c.num_cus);
+  if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "device query failed: %s", hipGetErrorString(e));
+
+  if (nranks <= kInlineRanks) {
+    for (int r = 0; r < nranks; ++r) {
+      c.send.p[r] = sendbufs[r];
+      c.recv.p[r] = recvbufs[r];
+    }
+  } else {
+    const void** st = reinterpret_cast<const void**>(ws + lay.send_tab);
+    const void** rt = reinterpret_cast<const void**>(ws + lay.recv_tab);
+    e = upload_table(st, sendbufs, nranks, stream);
+    if (e == hipSuccess) e = upload_table(rt, const_cast<const void* const*>(recvbufs), nranks, stream);
+    if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "pointer table upload failed: %s", hipGetErrorString(e));
+    c.send.table = reinterpret_cast<const uint64_t*>(st);
+    c.recv.table = reinterpret_cast<const uint64_t*>(rt);
+  }
+
+  if (sched == CCL_SIM_DIRECT) {
+    e = run_direct(c);
+  } else if (sched == CCL_SIM_RING_STEPWISE) {
+    e = run_ring_stepwise(c);
+  } else {
+    bool unsupported = false;
+    e = run_ring_persistent(c, &unsupported);
+    if (e == hipSuccess && unsupported)
+      return fail(CCL_SIM_UNSUPPORTED, "no co-resident grid for the persistent ring kernel on this device");
+  }
+  if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  return CCL_SIM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+ccl_sim_result_t ccl_sim_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                        size_t sendcount, size_t recvcount, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
+                                        ccl_sim_schedule_t schedule, void* workspace, size_t workspace_bytes,
+                                        ccl_sim_stream_t stream) {
+  return run_collective(CCL_SIM_COLL_REDUCE_SCATTER, sendbufs, recvbufs, nranks, sendcount, recvcount, dtype, op,
+                        schedule, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+ccl_sim_result_t ccl_sim_all_gather(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t sendcount,
+                                    size_t recvcount, ccl_sim_dtype_t dtype, ccl_sim_schedule_t schedule,
+                                    void* workspace, size_t workspace_bytes, ccl_sim_stream_t stream) {
+  return run_collective(CCL_SIM_COLL_ALL_GATHER, sendbufs, recvbufs, nranks, sendcount, recvcount, dtype, CCL_SIM_SUM,
+                        schedule, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+ccl_sim_result_t ccl_sim_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                                   ccl_sim_dtype_t dtype, ccl_sim_op_t op, ccl_sim_schedule_t schedule,
+                                   void* workspace, size_t workspace_bytes, ccl_sim_stream_t stream) {
+  return run_collective(CCL_SIM_COLL_ALLREDUCE, sendbufs, recvbufs, nranks, count, count, dtype, op, schedule,
+                        workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts, int nranks, size_t count,
+                                      size_t padded_count, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
+                                      ccl_sim_stream_t stream) {
+  g_last_error.clear();
+  if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS)
+    return fail(CCL_SIM_INVALID_ARGUMENT, "nranks=%d outside [1, %d]", nranks, CCL_SIM_MAX_RANKS);
+  if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", int(dtype));
+  if (!valid_op(op)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid op %d", int(op));
+  if (padded_count < count)
+    return fail(CCL_SIM_INVALID_ARGUMENT, "padded_count=%zu is smaller than count=%zu", padded_count, count);
+  const size_t es = elem_size(dtype);
+  uint64_t tmp = 0;
+  if (__builtin_mul_overflow(uint64_t(padded_count), uint64_t(es), &tmp))
+    return fail(CCL_SIM_INVALID_ARGUMENT, "buffer size in bytes overflows");
+  if (padded_count == 0) return CCL_SIM_SUCCESS;
+  ccl_sim_result_t rc = CCL_SIM_SUCCESS;
+  if (count > 0) {
+    rc = check_ptrs(srcs, nranks, "srcs", es);
+    if (rc != CCL_SIM_SUCCESS) return rc;
+  }
+  rc = check_ptrs(const_cast<const void* const*>(dsts), nranks, "dsts", es);
+  if (rc != CCL_SIM_SUCCESS) return rc;
+  std::vector<Span> ins, outs(nranks);
+  for (int r = 0; r < nranks; ++r) {
+    const uintptr_t d = reinterpret_cast<uintptr_t>(dsts[r]);
+    outs[r] = Span{d, d + padded_count * es, r};
+    if (count > 0) {
+      const uintptr_t s = reinterpret_cast<uintptr_t>(srcs[r]);
+      ins.push_back(Span{s, s + count * es, r});
+    }
+  }
+  std::string why;
+  auto same = [&](int r) { return count == 0 || srcs[r] == dsts[r]; };
+  if (!overlap_ok(outs, ins, same, &why)) return fail(CCL_SIM_INVALID_ARGUMENT, "%s", why.c_str());
+
+  Call c;
+  c.dtype = dtype;
+  c.op = op;
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = device_cus(&c.num_cus);
+  if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "device query failed: %s", hipGetErrorString(e));
+  for (int base = 0; base < nranks; base += kInlineRanks) {
+    const int n = std::min(kInlineRanks, nranks - base);
+    c.nranks = n;
+    for (int i = 0; i < n; ++i) {
+      c.send.p[i] = count > 0 ? srcs[base + i] : dsts[base + i];
+      c.recv.p[i] = dsts[base + i];
+    }
+    e = run_pad(c, count, padded_count);
+    if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return CCL_SIM_SUCCESS;
+}
+
+size_t ccl_sim_workspace_size(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_dtype_t dtype,
+                              ccl_sim_schedule_t schedule) {
+  if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS || !valid_dtype(dtype) || !valid_sched(schedule))
+    return SIZE_MAX;
+  const Layout l = layout(coll, nranks, count, dtype, schedule);
+  return l.ok ? l.total : SIZE_MAX;
+}
+
+uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_dtype_t dtype,
+                                   ccl_sim_schedule_t schedule) {
+  if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS || !valid_dtype(dtype) || !valid_sched(schedule))
+    return 0;
+  const uint64_t n = uint64_t(nranks), m = count, s = elem_size(dtype), a = accum_size(dtype);
+  const int sched = effective_schedule(nranks, schedule);
+  if (sched == CCL_SIM_DIRECT) {
+    if (coll == CCL_SIM_COLL_ALLREDUCE) return 2 * n * m * s;
+    return (n + 1) * m * s;
+  }
+  if (coll == CCL_SIM_COLL_ALL_GATHER) return 2 * n * m * s;
+  // ReduceScatter phase: per step every position reads the incoming partial
+  // (stored type at the first step) and the own element, and writes the new
+  // partial (stored type at the last step).
+  uint64_t per_pos = 0;
+  for (int t = 0; t + 1 < nranks; ++t) {
+    const uint64_t in = (t == 0) ? s : a;
+    const uint64_t out = (t == nranks - 2) ? s : a;
+    per_pos += in + s + out;
+  }
+  uint64_t bytes = per_pos * m;
+  if (coll == CCL_SIM_COLL_ALLREDUCE) bytes += 2 * (n - 1) * m * s;
+  return bytes;
+}
+
+int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_schedule_t schedule, int in_place) {
+  if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS || !valid_sched(schedule)) return -1;
+  if (count == 0) return 0;
+  const int sched = effective_schedule(nranks, schedule);
+  if (sched == CCL_SIM_DIRECT || sched == CCL_SIM_RING_PERSISTENT) return 1;
+  if (coll == CCL_SIM_COLL_ALLREDUCE) return 2 * (nranks - 1);
+  if (coll == CCL_SIM_COLL_REDUCE_SCATTER) return nranks - 1;
+  return in_place ? nranks - 1 : nranks;
+}
+
+int ccl_sim_ring_owner(int nranks, int rank) {
+  if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS || rank < 0 || rank >= nranks) return -1;
+  return (rank + 1) % nranks;
+}
+
+ccl_sim_result_t ccl_sim_ring_route(int nranks, int phase, int step, int rank, int* send_chunk, int* recv_chunk) {
+  if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS || rank < 0 || rank >= nranks || step < 0 || step > nranks - 2 ||
+      phase < 0 || phase > 2 || send_chunk == nullptr || recv_chunk == nullptr)
+    return CCL_SIM_INVALID_ARGUMENT;
+  const int owner = (phase == 1) ? 1 : 0;  // phase 0 and 2 share the (r - t, r - 1 - t) form
+  auto mod = [nranks](int x) { return ((x % nranks) + nranks) % nranks; };
+  *send_chunk = mod(rank + owner - step);
+  *recv_chunk = mod(rank + owner - 1 - step);
+  return CCL_SIM_SUCCESS;
+}
+
+const char* ccl_sim_result_string(ccl_sim_result_t result) {
+  switch (result) {
+    case CCL_SIM_SUCCESS: return "success";
+    case CCL_SIM_INVALID_ARGUMENT: return "invalid argument";
+    case CCL_SIM_UNSUPPORTED: return "unsupported on this device";
+    case CCL_SIM_INSUFFICIENT_WORKSPACE: return "insufficient workspace";
+    case CCL_SIM_HIP_ERROR: return "HIP runtime error";
+    case CCL_SIM_CAPACITY_MISMATCH: return "capacity mismatch";
+    default: return "unknown result code";
+  }
+}
+
+const char* ccl_sim_last_error(void) { return g_last_error.c_str(); }
+
+int ccl_sim_version(void) { return CCL_SIM_VERSION; }
+
+}  // extern "C"

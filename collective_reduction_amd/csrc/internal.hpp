@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI front end (api.cpp: validation and
+// planning) and the kernels (kernels.hip: launches).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace ccl {
+
+enum Coll : int { kReduceScatter = 0, kAllGather = 1, kAllReduce = 2 };
+enum DT : int { kInt32 = 0, kInt64 = 1, kFloat32 = 2, kBFloat16 = 3 };
+enum Sched : int { kDirect = 0, kRingStepwise = 1, kRingPersistent = 2 };
+
+// Everything a launch needs, already validated.
+struct Call {
+  int coll = 0, dtype = 0, op = 0, schedule = 0;
+  int nranks = 0;
+  uint64_t q = 0;          // shard (= ring chunk) length in elements
+  uint64_t limit = 0;      // positions >= limit are padding (AllReduce) or trimmed (AllGather)
+  bool in_place = false;   // AllGather: sendbufs[r] == recvbufs[r] + r·sendcount for every r
+  RankPtrs send{}, recv{};
+  void* partial = nullptr; // ring partials: [2][nranks][q] accumulators
+  unsigned* ctrl = nullptr;// persistent ring: barrier counter and abort flag
+  hipStream_t stream = nullptr;
+  int num_cus = 0;
+};
+
+// Control block layout (unsigned words) at the start of the workspace.
+enum CtrlWord : int { kCtrlBarrier = 0, kCtrlAbort = 1, kCtrlWords = 64 };
+
+hipError_t run_direct(const Call& c);
+hipError_t run_ring_stepwise(const Call& c);
+// Sets *unsupported when no co-resident grid can be formed.
+hipError_t run_ring_persistent(const Call& c, bool* unsupported);
+hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded);
+// Copy `n` host-side pointers into a device table on the stream (kernel
+// arguments carry them; no host-to-device memcpy).
+hipError_t upload_table(const void** dev_table, const void* const* host_ptrs, int n, hipStream_t stream);
+
+size_t elem_size(int dtype);
+size_t accum_size(int dtype);
+
+}  // namespace ccl

@@ -1,0 +1,769 @@
+// HIP kernels for gfx950: fused N-way reduce (ReduceScatter), broadcast-copy
+// (AllGather), fused AllReduce, ring steps (one launch per step, or one
+// persistent cooperative kernel with a grid barrier), identity padding.
+//
+// Pages cited:
+//   [DECOMP] "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
+//   [RING]   "Ring AllReduce 核心流程：梯度是怎么聚合的"
+//   [PRIMS]  "通信与互联（01）：集合通信原语与代价模型——α-β 模型与 ring all-reduce"
+//   [WHY-EQ] "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
+//
+// Work decomposition.  Every kernel is a grid-stride loop over tiles of
+// kBlock·V·kUnroll elements (V = 16 / sizeof(element): one 128-bit access
+// per lane per vector).  A tile never crosses a shard (or ring chunk)
+// boundary, so the shard a tile belongs to is one scalar division per tile
+// and the shard-local side of every access keeps the buffer's alignment;
+// the other side (the input of ReduceScatter at r·q + j, the output of
+// AllGather at s·q + j) is off a 16-byte boundary when q·sizeof(element)
+// is not a multiple of 16, which the unaligned 128-bit accesses absorb.  A
+// tile that lies wholly inside the valid range runs without per-lane
+// checks; in the last tile of a shard, lanes past the end of the shard, of
+// the logical length (padding) or of a trimmed output move fewer elements,
+// one at a time.
+//
+// Nothing here is a contraction: the kernels stream HBM at roughly one
+// combine per element loaded, so the only roofline that matters is HBM
+// bandwidth and MFMA plays no part.
+
+#include "internal.hpp"
+
+namespace ccl {
+namespace {
+
+#define CCL_GLOBAL __attribute__((address_space(1)))
+
+template <class T>
+constexpr int vec_elems() {
+  return 16 / static_cast<int>(sizeof(typename T::S));
+}
+
+constexpr uint64_t tile_of(int v) { return uint64_t(kBlock) * uint64_t(v) * kUnroll; }
+
+// K elements of E as one vector value, promising only element alignment.
+// gfx950 under the HSA runtime accepts unaligned global accesses, so the
+// compiler still emits whole 128-bit global loads and stores for these; a
+// shard that starts off a 16-byte boundary (q·sizeof(E) not a multiple of
+// 16) costs at most one extra cache line per wave, not a slower path.
+template <class E, int K>
+struct VecOf {
+  typedef E __attribute__((ext_vector_type(K), aligned(sizeof(E)))) type;
+};
+
+// Accesses go through global-address-space pointers so they compile to
+// global_load / global_store rather than flat accesses.
+template <class E, int K>
+__device__ inline typename VecOf<E, K>::type vload(const E* p) {
+  return *(const CCL_GLOBAL typename VecOf<E, K>::type*)(p);
+}
+template <class E, int K>
+__device__ inline void vstore(E* p, typename VecOf<E, K>::type v) {
+  *(CCL_GLOBAL typename VecOf<E, K>::type*)(p) = v;
+}
+template <class E>
+__device__ inline E get1(const E* p) {
+  return *(const CCL_GLOBAL E*)(p);
+}
+template <class E>
+__device__ inline void put1(E* p, E v) {
+  *(CCL_GLOBAL E*)(p) = v;
+}
+
+__device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
+  return j < len ? static_cast<int>(len - j < static_cast<uint64_t>(v) ? len - j : static_cast<uint64_t>(v)) : 0;
+}
+
+// One lane's kUnroll vectors inside a tile.  FULL: the whole tile lies
+// inside the valid range, so every vector is complete and no lane checks a
+// count; otherwise each vector carries its count of valid elements (0..V)
+// and incomplete ones move element by element.
+template <class T, bool FULL>
+struct Lane {
+  using S = typename T::S;
+  using A = typename T::A;
+  static constexpr int V = vec_elems<T>();
+  using SV = typename VecOf<S, V>::type;
+  using AV = typename VecOf<A, V>::type;
+  uint64_t j[kUnroll];
+  int cnt[kUnroll];
+
+  __device__ Lane(uint64_t seg, uint64_t len) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      j[u] = seg * tile_of(V) + uint64_t(u * kBlock + static_cast<int>(threadIdx.x)) * V;
+      cnt[u] = FULL ? V : lane_count(j[u], len, V);
+    }
+  }
+  __device__ bool on(int u) const { return FULL || cnt[u] > 0; }
+  __device__ bool whole(int u) const { return FULL || cnt[u] == V; }
+
+  __device__ SV load(const S* base, int u) const {
+    if (whole(u)) return vload<S, V>(base + j[u]);
+    SV v = {};
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (k < cnt[u]) v[k] = get1(base + j[u] + k);
+    return v;
+  }
+  __device__ void store(S* base, int u, SV v) const {
+    if (whole(u)) {
+      vstore<S, V>(base + j[u], v);
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (k < cnt[u]) put1(base + j[u] + k, static_cast<S>(v[k]));
+  }
+  __device__ AV load_acc(const A* base, int u) const {
+    if (whole(u)) return vload<A, V>(base + j[u]);
+    AV v = {};
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (k < cnt[u]) v[k] = get1(base + j[u] + k);
+    return v;
+  }
+  __device__ void store_acc(A* base, int u, AV v) const {
+    if (whole(u)) {
+      vstore<A, V>(base + j[u], v);
+      return;
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+      if (k < cnt[u]) put1(base + j[u] + k, static_cast<A>(v[k]));
+  }
+};
+
+template <class T>
+__device__ inline typename T::S* out_ptr(const RankPtrs& p, int r) {
+  return static_cast<typename T::S*>(const_cast<void*>(p.get(r)));
+}
+
+template <class T>
+__device__ inline const typename T::S* in_ptr(const RankPtrs& p, int r) {
+  return static_cast<const typename T::S*>(p.get(r));
+}
+
+// acc[u][k] = x^(0) ⊕ x^(1) ⊕ ... ⊕ x^(N-1) at offset off + j[u] + k, folded
+// strictly in ascending rank order.  Loads of kRankBatch ranks are issued
+// before any of them is combined, so each lane keeps up to
+// kRankBatch·kUnroll 128-bit loads in flight; the order of the combines is
+// still x^(0), x^(1), ... regardless.
+template <class T, int OP, bool FULL>
+__device__ inline void fold_ranks(const RankPtrs& src, int nranks, uint64_t off, const Lane<T, FULL>& ln,
+                                  typename T::A (&acc)[kUnroll][vec_elems<T>()]) {
+  constexpr int V = vec_elems<T>();
+  using SV = typename Lane<T, FULL>::SV;
+  for (int s0 = 0; s0 < nranks; s0 += kRankBatch) {
+    SV buf[kRankBatch][kUnroll];
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+      if (s0 + b < nranks) {
+        const typename T::S* p = in_ptr<T>(src, s0 + b) + off;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          if (ln.on(u)) buf[b][u] = ln.load(p, u);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) {
+      if (s0 + b < nranks) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            const typename T::A x = T::widen(buf[b][u][k]);
+            acc[u][k] = (s0 + b == 0) ? x : combine<T, OP>(acc[u][k], x);
+          }
+      }
+    }
+  }
+}
+
+template <class T, bool FULL>
+__device__ inline typename Lane<T, FULL>::SV narrow_vec(const typename T::A (&acc)[vec_elems<T>()]) {
+  typename Lane<T, FULL>::SV v;
+#pragma unroll
+  for (int k = 0; k < vec_elems<T>(); ++k) v[k] = T::narrow(acc[k]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Direct schedule.
+// ---------------------------------------------------------------------------
+struct ShardArgs {
+  RankPtrs send, recv;
+  int nranks;
+  uint64_t q;                // shard length
+  uint64_t tiles_per_shard;  // ceil(q / tile)
+  uint64_t ntiles;           // nranks · tiles_per_shard
+  uint64_t limit;            // AllGather: recvcount (positions at or past it are trimmed)
+};
+
+// ReduceScatter: recv[r][j] = ⊕_s send[s][r·q + j] ([DECOMP] §数学证明;
+// [RS-PAGE] equation rs-semantic-output).  One pass over the N inputs, one
+// write of the shards: (N+1)·M elements of HBM traffic.
+template <class T, int OP, bool FULL>
+__device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
+  constexpr int V = vec_elems<T>();
+  const Lane<T, FULL> ln(seg, a.q);
+  typename T::A acc[kUnroll][V];
+  fold_ranks<T, OP, FULL>(a.send, a.nranks, uint64_t(r) * a.q, ln, acc);
+  typename T::S* out = out_ptr<T>(a.recv, r);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ln.on(u)) ln.store(out, u, narrow_vec<T, FULL>(acc[u]));
+}
+
+template <class T, int OP>
+__global__ __launch_bounds__(kBlock) void rs_direct_kernel(ShardArgs a) {
+  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int r = static_cast<int>(tile / a.tiles_per_shard);
+    const uint64_t seg = tile - uint64_t(r) * a.tiles_per_shard;
+    if ((seg + 1) * kTile <= a.q)
+      rs_tile<T, OP, true>(a, r, seg);
+    else
+      rs_tile<T, OP, false>(a, r, seg);
+  }
+}
+
+// AllGather: recv[r][s·q + j] = send[s][j] for every r, positions below
+// `limit` only ([DECOMP] §数学证明 AllGather, trim of §Contract 实验四).
+// Each shard vector is read once into registers and stored N times.
+template <class T, bool FULL>
+__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
+  using SV = typename Lane<T, FULL>::SV;
+  const Lane<T, FULL> ln(seg, len);
+  const uint64_t base = uint64_t(s) * a.q;
+  const typename T::S* src = in_ptr<T>(a.send, s);
+  SV v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ln.on(u)) v[u] = ln.load(src, u);
+  for (int r = 0; r < a.nranks; ++r) {
+    typename T::S* dst = out_ptr<T>(a.recv, r) + base;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ln.on(u)) ln.store(dst, u, v[u]);
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(kBlock) void ag_direct_kernel(ShardArgs a) {
+  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int s = static_cast<int>(tile / a.tiles_per_shard);
+    const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
+    const uint64_t base = uint64_t(s) * a.q;
+    const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+    if ((seg + 1) * kTile <= len)
+      ag_tile<T, true>(a, s, seg, len);
+    else
+      ag_tile<T, false>(a, s, seg, len);
+  }
+}
+
+struct FlatArgs {
+  RankPtrs send, recv;
+  int nranks;
+  uint64_t count;
+  uint64_t ntiles;
+};
+
+// Direct AllReduce in one kernel: y^(r)_i = ⊕_s x^(s)_i stored to all N
+// outputs ([DECOMP] §数学证明 Direct AllReduce): 2N·M elements of traffic.
+template <class T, int OP, bool FULL>
+__device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
+  using SV = typename Lane<T, FULL>::SV;
+  constexpr int V = vec_elems<T>();
+  const Lane<T, FULL> ln(tile, a.count);
+  typename T::A acc[kUnroll][V];
+  fold_ranks<T, OP, FULL>(a.send, a.nranks, 0, ln, acc);
+  SV o[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) o[u] = narrow_vec<T, FULL>(acc[u]);
+  for (int r = 0; r < a.nranks; ++r) {
+    typename T::S* dst = out_ptr<T>(a.recv, r);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ln.on(u)) ln.store(dst, u, o[u]);
+  }
+}
+
+template <class T, int OP>
+__global__ __launch_bounds__(kBlock) void ar_direct_kernel(FlatArgs a) {
+  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    if ((tile + 1) * kTile <= a.count)
+      ar_tile<T, OP, true>(a, tile);
+    else
+      ar_tile<T, OP, false>(a, tile);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ring schedule ([RING] §1 and pseudocode; [PRIMS] §五.2-五.3).
+//
+// Global step numbering of one call:
+//   AllReduce      steps 0..N-2 ReduceScatter phase (t = step),
+//                  steps N-1..2N-3 AllGather phase (t = step - (N-1));
+//   ReduceScatter  steps 0..N-2;
+//   AllGather      step 0 places each rank's own shard, steps 1..N-1 copy.
+// Each step is N independent transfers, one per rank; a tile belongs to one
+// rank's transfer.  "Send" and "receive" are HBM reads of the upstream
+// rank's data; the ReduceScatter phase's in-flight partials live in a
+// double buffer P[2][N][q] of accumulators (rank r's slot of step t is read
+// by rank r+1 at step t+1, so two generations are live at once).
+// ---------------------------------------------------------------------------
+struct RingArgs {
+  RankPtrs send, recv;
+  int nranks;
+  int coll;
+  int step;                  // the step a stepwise launch runs
+  int first_step;            // persistent: 1 skips an in-place AllGather's placement
+  uint64_t q;                // chunk length
+  uint64_t limit;            // positions at or past it are padding / trimmed
+  uint64_t tiles_per_chunk;
+  uint64_t ntiles;           // nranks · tiles_per_chunk
+  void* partial;
+  unsigned* ctrl;
+  unsigned spin_limit;
+};
+
+__device__ inline int mod_n(int x, int n) {
+  x %= n;
+  return x < 0 ? x + n : x;
+}
+
+__device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
+  const uint64_t base = uint64_t(c) * a.q;
+  if (base >= a.limit) return 0;
+  return a.limit - base < a.q ? a.limit - base : a.q;
+}
+
+// ReduceScatter step t for rank r: receive chunk c = (r-1-t) from rank r-1
+// and combine the rank's own x^(r) chunk into it (incoming partial on the
+// left, so chunk c folds x^(c), x^(c+1), ...).  At t = 0 the incoming
+// partial is rank r-1's own input; at the last step t = N-2 the completed
+// chunk is stored as output instead of a partial: AllReduce into
+// out_r[chunk c] (the AllGather phase's source: the phase boundary fused
+// in one state machine as in [DECOMP] §源码三), ReduceScatter into
+// recvbufs[c], c = r+1.
+template <class T, int OP, bool FULL>
+__device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len) {
+  using A = typename T::A;
+  using L = Lane<T, FULL>;
+  constexpr int V = vec_elems<T>();
+  const int n = a.nranks;
+  const int up = mod_n(r - 1, n);
+  const uint64_t cbase = uint64_t(c) * a.q;
+  const bool last = (t == n - 2);
+  A* part = static_cast<A*>(a.partial);
+  const uint64_t slot = uint64_t(n) * a.q;  // elements per generation
+  const L ln(seg, len);
+  typename L::AV in[kUnroll];
+  typename L::SV own[kUnroll];
+  const typename T::S* mine = in_ptr<T>(a.send, r) + cbase;
+  if (t == 0) {
+    const typename T::S* theirs = in_ptr<T>(a.send, up) + cbase;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ln.on(u)) {
+        const typename L::SV x = ln.load(theirs, u);
+#pragma unroll
+        for (int k = 0; k < V; ++k) in[u][k] = T::widen(x[k]);
+      }
+  } else {
+    const A* theirs = part + uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (ln.on(u)) in[u] = ln.load_acc(theirs, u);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ln.on(u)) own[u] = ln.load(mine, u);
+  if (!last) {
+    A* dst = part + uint64_t(t & 1) * slot + uint64_t(r) * a.q;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!ln.on(u)) continue;
+      typename L::AV v;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = combine<T, OP>(in[u][k], T::widen(own[u][k]));
+      ln.store_acc(dst, u, v);
+    }
+  } else {
+    typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, r) + cbase : out_ptr<T>(a.recv, c);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (!ln.on(u)) continue;
+      typename L::SV v;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = T::narrow(combine<T, OP>(in[u][k], T::widen(own[u][k])));
+      ln.store(dst, u, v);
+    }
+  }
+}
+
+// Copy of `len` elements from src to dst for one tile (AllGather steps and
+// the stand-alone AllGather's own-shard placement).
+template <class T, bool FULL>
+__device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, uint64_t seg, uint64_t len) {
+  using L = Lane<T, FULL>;
+  const L ln(seg, len);
+  typename L::SV v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ln.on(u)) v[u] = ln.load(src, u);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (ln.on(u)) ln.store(dst, u, v[u]);
+}
+
+template <class T, int OP>
+__device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
+  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  const int n = a.nranks;
+  const int r = static_cast<int>(tile / a.tiles_per_chunk);
+  const uint64_t seg = tile - uint64_t(r) * a.tiles_per_chunk;
+  int c;
+  bool reduce = false;
+  const typename T::S* src;
+  if (a.coll != kAllGather && step < n - 1) {
+    // ReduceScatter phase ([PRIMS] §五.2): receive chunk r-1-t.
+    reduce = true;
+    c = mod_n(r - 1 - step, n);
+    src = nullptr;
+  } else if (a.coll == kAllGather && step == 0) {
+    // Stand-alone AllGather: rank r's own shard into its chunk r
+    // (the directCopySend of [DECOMP] §源码四).
+    c = r;
+    src = in_ptr<T>(a.send, r);
+  } else {
+    // AllGather phase ([PRIMS] §五.3): receive chunk c from rank r-1 and
+    // overwrite the local copy.  After the ring ReduceScatter phase rank r
+    // owns chunk r+1, so it receives chunk r-t; a stand-alone AllGather's
+    // rank r owns chunk r and receives chunk r-1-t.
+    const int t = (a.coll == kAllGather) ? step - 1 : step - (n - 1);
+    const int owner = (a.coll == kAllGather) ? 0 : 1;
+    c = mod_n(r + owner - 1 - t, n);
+    src = in_ptr<T>(a.recv, mod_n(r - 1, n)) + uint64_t(c) * a.q;
+  }
+  const uint64_t len = chunk_len(a, c);
+  const bool full = (seg + 1) * kTile <= len;
+  if (reduce) {
+    if (full)
+      ring_rs_tile<T, OP, true>(a, step, r, seg, c, len);
+    else
+      ring_rs_tile<T, OP, false>(a, step, r, seg, c, len);
+  } else {
+    typename T::S* dst = out_ptr<T>(a.recv, r) + uint64_t(c) * a.q;
+    if (full)
+      copy_tile<T, true>(src, dst, seg, len);
+    else
+      copy_tile<T, false>(src, dst, seg, len);
+  }
+}
+
+template <class T, int OP>
+__global__ __launch_bounds__(kBlock) void ring_step_kernel(RingArgs a) {
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP>(a, a.step, tile);
+}
+
+// Grid-wide barrier for the persistent ring.  Every workgroup of the grid
+// is co-resident (cooperative launch), arrives once per step on a counter
+// that only grows, and waits until all gridDim.x arrivals of this step are
+// in.  Every wave fences at device scope before the arrival (its stores are
+// complete and written back out of its XCD's L2) and again after the wait
+// (stale lines are dropped), so a workgroup's HBM stores of one step are
+// seen by every other workgroup's loads of the next, across all eight XCDs
+// and their separate L2 caches.  The wait is bounded: after spin_limit polls
+// it raises the abort word, and every workgroup that sees the word stops,
+// so the grid always drains.
+__device__ inline bool grid_barrier(unsigned* ctrl, unsigned target, unsigned spin_limit) {
+  __shared__ int s_ok;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(ctrl + kCtrlAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
+          ++spins > spin_limit) {
+        __hip_atomic_store(ctrl + kCtrlAbort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  __threadfence();
+  return s_ok != 0;
+}
+
+template <class T, int OP>
+__global__ __launch_bounds__(kBlock) void ring_persistent_kernel(RingArgs a) {
+  const int n = a.nranks;
+  const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
+  unsigned arrivals = 0;
+  for (int step = a.first_step; step < nsteps; ++step) {
+    if (step > a.first_step) {
+      arrivals += gridDim.x;
+      if (!grid_barrier(a.ctrl, arrivals, a.spin_limit)) return;
+    }
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP>(a, step, tile);
+  }
+}
+
+__global__ void reset_ctrl_kernel(unsigned* ctrl) {
+  if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Identity padding ([DECOMP] condition three): dst = src for i < count,
+// identity(op) for count <= i < padded.
+// ---------------------------------------------------------------------------
+struct PadArgs {
+  RankPtrs src, dst;
+  int nranks;
+  uint64_t count, padded, tiles_per_rank, ntiles;
+};
+
+template <class T, int OP>
+__global__ __launch_bounds__(kBlock) void pad_kernel(PadArgs a) {
+  using S = typename T::S;
+  constexpr int V = vec_elems<T>();
+  constexpr uint64_t kTile = uint64_t(kBlock) * V;
+  const S ident = T::narrow(identity<T, OP>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int r = static_cast<int>(tile / a.tiles_per_rank);
+    const uint64_t seg = tile - uint64_t(r) * a.tiles_per_rank;
+    const S* src = in_ptr<T>(a.src, r);
+    S* dst = out_ptr<T>(a.dst, r);
+    const uint64_t j = seg * kTile + uint64_t(threadIdx.x) * V;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      const uint64_t i = j + k;
+      if (i < a.count) {
+        if (src != dst) dst[i] = src[i];
+      } else if (i < a.padded) {
+        dst[i] = ident;
+      }
+    }
+  }
+}
+
+struct TableArgs {
+  const void* p[kInlineRanks];
+  const void** dst;
+  int n;
+};
+
+__global__ void store_table_kernel(TableArgs a) {
+  if (static_cast<int>(threadIdx.x) < a.n) a.dst[threadIdx.x] = a.p[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+// ---------------------------------------------------------------------------
+template <class F>
+hipError_t by_type(int dtype, F&& f) {
+  switch (dtype) {
+    case kInt32: return f.template operator()<I32>();
+    case kInt64: return f.template operator()<I64>();
+    case kFloat32: return f.template operator()<F32>();
+    case kBFloat16: return f.template operator()<BF16>();
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T, class F>
+hipError_t by_op(int op, F&& f) {
+  switch (op) {
+    case kSum: return f.template operator()<T, kSum>();
+    case kProd: return f.template operator()<T, kProd>();
+    case kMax: return f.template operator()<T, kMax>();
+    case kMin: return f.template operator()<T, kMin>();
+    default: return hipErrorInvalidValue;
+  }
+}
+
+#ifndef CCL_SIM_BLOCKS_PER_CU
+#define CCL_SIM_BLOCKS_PER_CU 64
+#endif
+
+unsigned grid_for(uint64_t ntiles, int num_cus) {
+  const uint64_t cap = uint64_t(num_cus > 0 ? num_cus : 256) * CCL_SIM_BLOCKS_PER_CU;
+  const uint64_t g = ntiles < cap ? ntiles : cap;
+  return static_cast<unsigned>(g > 0 ? g : 1);
+}
+
+template <class T>
+uint64_t tile_elems() {
+  return uint64_t(kBlock) * vec_elems<T>() * kUnroll;
+}
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+RingArgs make_ring_args(const Call& c, uint64_t tile) {
+  RingArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.coll = c.coll;
+  a.q = c.q;
+  a.limit = c.limit;
+  a.tiles_per_chunk = ceil_div(c.q, tile);
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_chunk;
+  a.partial = c.partial;
+  a.ctrl = c.ctrl;
+  a.spin_limit = 1u << 22;
+  return a;
+}
+
+}  // namespace
+
+size_t elem_size(int dtype) {
+  switch (dtype) {
+    case kInt32: return 4;
+    case kInt64: return 8;
+    case kFloat32: return 4;
+    case kBFloat16: return 2;
+    default: return 0;
+  }
+}
+
+size_t accum_size(int dtype) { return dtype == kBFloat16 ? 4 : elem_size(dtype); }
+
+hipError_t run_direct(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const uint64_t tile = tile_elems<T>();
+    if (c.coll == kAllReduce) {
+      FlatArgs a{};
+      a.send = c.send;
+      a.recv = c.recv;
+      a.nranks = c.nranks;
+      a.count = c.limit;
+      a.ntiles = ceil_div(c.limit, tile);
+      const unsigned grid = grid_for(a.ntiles, c.num_cus);
+      return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
+        hipLaunchKernelGGL((ar_direct_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        return hipGetLastError();
+      });
+    }
+    ShardArgs a{};
+    a.send = c.send;
+    a.recv = c.recv;
+    a.nranks = c.nranks;
+    a.q = c.q;
+    a.tiles_per_shard = ceil_div(c.q, tile);
+    a.ntiles = uint64_t(c.nranks) * a.tiles_per_shard;
+    a.limit = c.limit;
+    const unsigned grid = grid_for(a.ntiles, c.num_cus);
+    if (c.coll == kReduceScatter) {
+      return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
+        hipLaunchKernelGGL((rs_direct_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        return hipGetLastError();
+      });
+    }
+    hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t run_ring_stepwise(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    RingArgs a = make_ring_args(c, tile_elems<T>());
+    const unsigned grid = grid_for(a.ntiles, c.num_cus);
+    const int n = c.nranks;
+    const int nsteps = (c.coll == kAllReduce) ? 2 * (n - 1) : (c.coll == kReduceScatter ? n - 1 : n);
+    const int first = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      for (int step = first; step < nsteps; ++step) {
+        a.step = step;
+        hipLaunchKernelGGL((ring_step_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    });
+  });
+}
+
+hipError_t run_ring_persistent(const Call& c, bool* unsupported) {
+  *unsupported = false;
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    RingArgs a = make_ring_args(c, tile_elems<T>());
+    a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      auto kernel = ring_persistent_kernel<U, OP>;
+      int per_cu = 0;
+      hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
+      if (e != hipSuccess) return e;
+      if (per_cu <= 0 || c.num_cus <= 0) {
+        *unsupported = true;
+        return hipSuccess;
+      }
+      uint64_t grid = uint64_t(per_cu) * uint64_t(c.num_cus);
+      if (grid > a.ntiles) grid = a.ntiles;
+      if (grid == 0) grid = 1;
+      hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      void* args[] = {&a};
+      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)),
+                                     dim3(kBlock), args, 0, c.stream);
+      if (e == hipErrorCooperativeLaunchTooLarge) {
+        (void)hipGetLastError();
+        *unsupported = true;
+        return hipSuccess;
+      }
+      return e;
+    });
+  });
+}
+
+hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const uint64_t tile = uint64_t(kBlock) * vec_elems<T>();
+    PadArgs a{};
+    a.src = c.send;
+    a.dst = c.recv;
+    a.nranks = c.nranks;
+    a.count = count;
+    a.padded = padded;
+    a.tiles_per_rank = ceil_div(padded, tile);
+    a.ntiles = uint64_t(c.nranks) * a.tiles_per_rank;
+    const unsigned grid = grid_for(a.ntiles, c.num_cus);
+    auto go = [&](auto kernel) -> hipError_t {
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, c.stream, a);
+      return hipGetLastError();
+    };
+    switch (c.op) {
+      case kSum: return go(pad_kernel<T, kSum>);
+      case kProd: return go(pad_kernel<T, kProd>);
+      case kMax: return go(pad_kernel<T, kMax>);
+      case kMin: return go(pad_kernel<T, kMin>);
+      default: return hipErrorInvalidValue;
+    }
+  });
+}
+
+hipError_t upload_table(const void** dev_table, const void* const* host_ptrs, int n, hipStream_t stream) {
+  for (int base = 0; base < n; base += kInlineRanks) {
+    TableArgs a{};
+    a.n = (n - base < kInlineRanks) ? n - base : kInlineRanks;
+    a.dst = dev_table + base;
+    for (int i = 0; i < a.n; ++i) a.p[i] = host_ptrs[base + i];
+    hipLaunchKernelGGL(store_table_kernel, dim3(1), dim3(kInlineRanks), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace ccl

@@ -78,18 +78,33 @@ def _draw_chunk(s, rank, chunk, dtype_override=None):
     raise ValueError(f"distribution {dist!r} does not produce {dtype}")
 
 
-def rank_buffer(s, rank, start=0, stop=None):
-    """Elements [start, stop) of rank ``rank``'s buffer for workload spec ``s``."""
+def rank_buffer(s, rank, start=0, stop=None, workers=1):
+    """Elements [start, stop) of rank ``rank``'s buffer for workload spec ``s``.
+
+    ``workers`` > 1 draws the chunks on that many threads (NumPy's generators
+    release the GIL while filling); the values do not depend on it.
+    """
     count = s["count"]
     stop = count if stop is None else min(stop, count)
+    out = np.empty(max(stop - start, 0), dtype=_STORAGE[s["dtype"]])
     if start >= stop:
-        return np.empty(0, dtype=_STORAGE[s["dtype"]])
-    parts = []
-    for c in range(start // CHUNK, (stop - 1) // CHUNK + 1):
+        return out
+    chunks = list(range(start // CHUNK, (stop - 1) // CHUNK + 1))
+
+    def fill(c):
         block = _draw_chunk(s, rank, c)
         base = c * CHUNK
-        parts.append(block[max(start - base, 0): stop - base])
-    return np.concatenate(parts)
+        lo, hi = max(start, base), min(stop, base + block.size)
+        out[lo - start:hi - start] = block[lo - base:hi - base]
+
+    if workers > 1 and len(chunks) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(workers, len(chunks))) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for c in chunks:
+            fill(c)
+    return out
 
 
 def all_buffers(s):

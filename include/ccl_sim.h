@@ -1,0 +1,261 @@
+/*
+ * ccl_sim.h — ReduceScatter, AllGather and AllReduce over N virtual ranks
+ * whose buffers all live in one AMD MI355X (gfx950) GPU's HBM.
+ *
+ * One call covers all N ranks, the way a single host process drives every
+ * rank with grouped calls in the Nsight probe of "NCCL 专家课程 07：AllReduce
+ * 等价分解、显存生命周期与 Kernel 证据" (blog.cptz.space), §Kernel 证据.  The
+ * "links" between ranks are HBM reads and writes; there is no second GPU.
+ *
+ * Pages cited below:
+ *   [DECOMP]  "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
+ *             (blog.cptz.space/posts/nccl-collective-decomposition/)
+ *   [WHY-EQ]  "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL
+ *             Ring AllReduce" (loosp.cn)
+ *   [RING]    "Ring AllReduce 核心流程：梯度是怎么聚合的" (llmnex.top)
+ *   [RS-PAGE] "ReduceScatter" (tier6-model.pages.dev, 集合通信)
+ *   [PRIMS]   "通信与互联（01）：集合通信原语与代价模型——α-β 模型与 ring
+ *             all-reduce" (arganzheng.life)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Buffers.   `sendbufs` and `recvbufs` are HOST arrays of `nranks` DEVICE
+ *            pointers; element r belongs to virtual rank r.  The caller
+ *            allocates and owns every device buffer, including `workspace`.
+ *            The library keeps no pointer after a call returns and allocates
+ *            no device memory.
+ * Layout.    Every rank buffer is a contiguous 1-D array of `dtype`
+ *            elements.  Element i of a full buffer belongs to shard i / q
+ *            (rank-major sharding, [DECOMP] §数学证明).
+ * Alignment. Pointers must be aligned to the element size.  16-byte aligned
+ *            pointers and shard sizes with q·sizeof(dtype) a multiple of 16
+ *            take the fastest path; any other layout is handled, slower.
+ * Streams.   Work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *            stream) and the call returns without waiting.  Buffers must stay
+ *            alive until that stream work completes ([DECOMP] §显存生命周期:
+ *            a buffer's lifetime ends with the last kernel that reads it).
+ * Workspace. Device scratch of at least ccl_sim_workspace_size(...) bytes,
+ *            256-byte aligned, owned by the caller.  It carries the device
+ *            copy of the pointer tables when nranks > 64, the partial sums
+ *            the ring schedules pass between ranks, and the grid-barrier
+ *            counter of the persistent ring.  Calls that share a workspace
+ *            must be ordered on one stream.  NULL is allowed when the
+ *            required size is 0.
+ * Errors.    Every argument is validated before any HIP call; on any error
+ *            nothing is enqueued and the output buffers are untouched (as the
+ *            capacity check of [DECOMP] §Contract 实验四 rejects a
+ *            non-divisible ReduceScatter on every rank before any kernel).
+ *            ccl_sim_last_error() returns a message naming the failed check.
+ *            A HIP failure while enqueueing returns CCL_SIM_HIP_ERROR.
+ *            Count 0 is a successful no-op.
+ * Overlap.   Output buffers must not overlap each other.  An output may
+ *            overlap an input only in the in-place forms:
+ *              AllReduce      recvbufs[r] == sendbufs[r]            ([DECOMP]
+ *                             §源码五: the AllReduce tensor is both input and
+ *                             output);
+ *              AllGather      sendbufs[r] == recvbufs[r] + r·sendcount
+ *                             ([DECOMP] §源码四, the in-place AllGather test);
+ *              ReduceScatter  recvbufs[r] == sendbufs[r] + r·recvcount (the
+ *                             dual of the AllGather form).
+ *            Inputs may alias each other (they are only read).
+ * Order.     Integer SUM / PROD wrap modulo 2^32 or 2^64; float32 SUM / PROD
+ *            results depend on the combining order ([DECOMP] §等价成立的条件,
+ *            condition five).  CCL_SIM_DIRECT folds ranks in ascending order
+ *            0, 1, ..., N-1.  The ring schedules fold chunk c in the ring's
+ *            order x^(c), x^(c+1), ..., x^(c-1).  Within one call all N
+ *            outputs are bit-identical.  bf16 is accumulated in float32 and
+ *            rounded to nearest even once, when a result is stored.
+ *            MAX / MIN keep the running partial on ties.
+ * Threads.   The library holds no mutable global state except a cached
+ *            per-device compute-unit count and a thread-local error
+ *            message; calls with distinct workspaces may run concurrently.
+ */
+#ifndef CCL_SIM_H
+#define CCL_SIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CCL_SIM_VERSION 100      /* 1.0.0 */
+#define CCL_SIM_MAX_RANKS 1024
+#define CCL_SIM_INLINE_RANKS 64  /* up to this many ranks need no pointer table in the workspace */
+
+typedef enum {
+  CCL_SIM_SUCCESS = 0,
+  CCL_SIM_INVALID_ARGUMENT = 1,      /* a check on counts, pointers, enums or overlap failed */
+  CCL_SIM_UNSUPPORTED = 2,           /* valid request this device cannot run (e.g. no co-resident grid) */
+  CCL_SIM_INSUFFICIENT_WORKSPACE = 3,/* workspace NULL or smaller than ccl_sim_workspace_size() */
+  CCL_SIM_HIP_ERROR = 4,             /* a HIP runtime call failed while enqueueing */
+  CCL_SIM_CAPACITY_MISMATCH = 5      /* ReduceScatter sendcount != nranks * recvcount */
+} ccl_sim_result_t;
+
+typedef enum {
+  CCL_SIM_INT32 = 0,
+  CCL_SIM_INT64 = 1,
+  CCL_SIM_FLOAT32 = 2,
+  CCL_SIM_BFLOAT16 = 3
+} ccl_sim_dtype_t;
+
+/* The reduction operators of [PRIMS] §二.1 (avg is not provided). */
+typedef enum {
+  CCL_SIM_SUM = 0,
+  CCL_SIM_PROD = 1,
+  CCL_SIM_MAX = 2,
+  CCL_SIM_MIN = 3
+} ccl_sim_op_t;
+
+typedef enum {
+  /* Read every input once: one fused kernel per collective. */
+  CCL_SIM_DIRECT = 0,
+  /* The ring of [RING] §1 / [PRIMS] §五: one kernel launch per ring step. */
+  CCL_SIM_RING_STEPWISE = 1,
+  /* The same ring steps inside one cooperative kernel, a grid-wide barrier
+   * between steps. */
+  CCL_SIM_RING_PERSISTENT = 2
+} ccl_sim_schedule_t;
+
+typedef enum {
+  CCL_SIM_COLL_REDUCE_SCATTER = 0,
+  CCL_SIM_COLL_ALL_GATHER = 1,
+  CCL_SIM_COLL_ALLREDUCE = 2
+} ccl_sim_coll_t;
+
+/* Same layout as hipStream_t; declared here so C callers need no HIP header. */
+typedef struct ihipStream_t* ccl_sim_stream_t;
+
+/*
+ * ReduceScatter, rank-major ([DECOMP] §数学证明 ReduceScatter; [RS-PAGE]
+ * §语义定义, equation rs-semantic-output):
+ *     recvbufs[r][j] = ⊕_{s=0}^{N-1} sendbufs[s][r·recvcount + j],
+ *     0 <= j < recvcount.
+ * sendbufs[s] holds sendcount elements, recvbufs[r] receives recvcount.
+ * The count rule is NCCL's ([DECOMP] §源码一): sendcount must equal
+ * nranks·recvcount, else CCL_SIM_CAPACITY_MISMATCH and nothing is enqueued
+ * ([DECOMP] §Contract 实验四).  A length that does not divide is padded first
+ * with ccl_sim_pad_identity.
+ * Ring schedules: N-1 steps; ring rank n ends holding chunk (n+1) mod N
+ * ([PRIMS] §五.2), which is stored as recvbufs[(n+1) mod N], so the result
+ * is rank-major for every schedule.
+ */
+ccl_sim_result_t ccl_sim_reduce_scatter(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                        size_t sendcount, size_t recvcount, ccl_sim_dtype_t dtype,
+                                        ccl_sim_op_t op, ccl_sim_schedule_t schedule, void* workspace,
+                                        size_t workspace_bytes, ccl_sim_stream_t stream);
+
+/*
+ * AllGather in source-rank order ([DECOMP] §数学证明 AllGather):
+ *     recvbufs[r][s·sendcount + j] = sendbufs[s][j]   for every r,
+ * keeping only the first recvcount elements of each output, so
+ * recvcount < nranks·sendcount trims a padded result back to its logical
+ * length ([DECOMP] §Contract 实验四).  recvcount > nranks·sendcount is
+ * CCL_SIM_CAPACITY_MISMATCH.  Bit-exact copy for every dtype.
+ * Ring schedules: rank r starts with shard r and N-1 recv-copy-send steps
+ * follow ([PRIMS] §五.3, [WHY-EQ] §6).
+ */
+ccl_sim_result_t ccl_sim_all_gather(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                    size_t sendcount, size_t recvcount, ccl_sim_dtype_t dtype,
+                                    ccl_sim_schedule_t schedule, void* workspace, size_t workspace_bytes,
+                                    ccl_sim_stream_t stream);
+
+/*
+ * AllReduce ([DECOMP] §数学证明 Direct AllReduce):
+ *     recvbufs[r][i] = ⊕_{s=0}^{N-1} sendbufs[s][i],  0 <= i < count,
+ * identical for every r.  Any count is accepted: positions past count in
+ * the last shard behave as the op's identity and are never stored (the
+ * pad-and-trim of [DECOMP] condition three, done without materialising it).
+ * CCL_SIM_DIRECT runs one fused kernel.  The ring schedules run the
+ * 2(N-1) steps of [RING] §1, the ReduceScatter phase's last step writing
+ * the completed chunk straight into the rank's output, which the AllGather
+ * phase then forwards ([DECOMP] §源码三, the phase boundary fused in one
+ * state machine).
+ */
+ccl_sim_result_t ccl_sim_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                                   ccl_sim_dtype_t dtype, ccl_sim_op_t op, ccl_sim_schedule_t schedule,
+                                   void* workspace, size_t workspace_bytes, ccl_sim_stream_t stream);
+
+/*
+ * Identity padding ([DECOMP] §等价成立的条件, condition three):
+ *     dsts[r][i] = srcs[r][i]     for i < count,
+ *     dsts[r][i] = identity(op)   for count <= i < padded_count,
+ * with identity 0 (SUM), 1 (PROD), -inf / INT_MIN (MAX), +inf / INT_MAX
+ * (MIN) — never a mechanical zero.  srcs[r] == dsts[r] only fills the tail.
+ * padded_count < count is CCL_SIM_INVALID_ARGUMENT.  No workspace needed.
+ */
+ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts, int nranks, size_t count,
+                                      size_t padded_count, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
+                                      ccl_sim_stream_t stream);
+
+/*
+ * In the two queries below `count` is M, the logical per-rank length of the
+ * full (unsharded) buffer: sendcount for ReduceScatter, recvcount for
+ * AllGather, count for AllReduce.  q = ceil(M / N) is the shard length.
+ *
+ * Workspace bytes one call needs (0 when none, SIZE_MAX for invalid
+ * arguments): the pointer tables when nranks > 64, the ring's double-
+ * buffered partials 2·N·q·a (a = accumulator size: 4 for bf16, else the
+ * element size) for ring ReduceScatter and ring AllReduce with N >= 3, and
+ * a barrier block for the persistent ring.
+ */
+size_t ccl_sim_workspace_size(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_dtype_t dtype,
+                              ccl_sim_schedule_t schedule);
+
+/*
+ * Algorithmic HBM bytes of one call: every element the schedule's data
+ * movement must read or write, counted once per access (the numerator of
+ * the effective bandwidth).  s = element size, a = accumulator size:
+ *   DIRECT  ReduceScatter (N+1)·M·s    AllGather (N+1)·M·s    AllReduce 2N·M·s
+ *   ring    ReduceScatter: per step, each of the M positions reads the
+ *           incoming partial and the rank's own element and writes the new
+ *           partial; the first step's incoming partial and the last step's
+ *           output are stored-type, the rest accumulator-type.  For 4- and
+ *           8-byte types this is 3(N-1)·M·s.
+ *           AllGather 2N·M·s (own shard placed, then N-1 copy steps).
+ *           AllReduce the ReduceScatter phase plus 2(N-1)·M·s.
+ * N = 1 runs the direct copy for every schedule.  Returns 0 for invalid
+ * arguments.
+ */
+uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_dtype_t dtype,
+                                   ccl_sim_schedule_t schedule);
+
+/* Compute-kernel launches one call enqueues for count > 0: DIRECT 1;
+ * stepwise ring N-1 (ReduceScatter), N-1 plus 1 own-shard placement
+ * (out-of-place AllGather), 2(N-1) (AllReduce) — the nsteps of [DECOMP]
+ * §源码二; persistent ring 1.  Not counted: the pointer-table uploads when
+ * nranks > 64 and the persistent ring's barrier reset.  N = 1: 1.
+ * Returns -1 for invalid arguments. */
+int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_schedule_t schedule,
+                         int in_place);
+
+/* Chunk ring rank `rank` holds complete after the ReduceScatter phase:
+ * (rank+1) mod nranks ([PRIMS] §五.2; [RING] §1).  -1 if out of range. */
+int ccl_sim_ring_owner(int nranks, int rank);
+
+/*
+ * Ring routing ([RING] §2 N=4 table and pseudocode; [PRIMS] §五.2-五.3):
+ * phase 0 = ReduceScatter, step t in [0, N-2]: send chunk (rank - t),
+ *           receive chunk (rank - 1 - t);
+ * phase 1 = AllGather after the ReduceScatter phase: send (rank + 1 - t),
+ *           receive (rank - t);
+ * phase 2 = stand-alone AllGather (rank r starts with shard r): send
+ *           (rank - t), receive (rank - 1 - t).
+ * All indices mod nranks.  Returns CCL_SIM_INVALID_ARGUMENT if out of range.
+ */
+ccl_sim_result_t ccl_sim_ring_route(int nranks, int phase, int step, int rank, int* send_chunk,
+                                    int* recv_chunk);
+
+const char* ccl_sim_result_string(ccl_sim_result_t result);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* ccl_sim_last_error(void);
+
+int ccl_sim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCL_SIM_H */

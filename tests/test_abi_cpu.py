@@ -1,0 +1,193 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, and rejects bad arguments before any HIP call (so these run without
+a GPU).  Device addresses here are fake integers: a rejected call never
+dereferences them."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cs():
+    from collective_reduction_amd import ccl_sim
+    return ccl_sim
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ccl_sim.h"), encoding="utf-8").read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(ccl_sim_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol(cs):
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(cs.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(cs.EXPORTED)
+    assert cs.ccl_sim_version() == 100
+
+
+BASE = 1 << 32
+
+
+def fake(n, count, es, stride=None, base=BASE):
+    stride = stride or ((count * es + 4095) // 4096 + 1) * 4096
+    return [base + r * stride for r in range(n)]
+
+
+def code_of(fn, *a, **k):
+    try:
+        fn(*a, **k)
+    except TypeError:
+        return "capacity"
+    except Exception as e:  # noqa: BLE001
+        return getattr(e, "code", str(e))
+    return 0
+
+
+def test_capacity_check_rejects_nondivisible_reduce_scatter(cs):
+    """1003 elements over 4 ranks with recvcount 250 is rejected with the
+    capacity-check message before anything runs."""
+    n = 4
+    with pytest.raises(TypeError, match="input tensor must be the same size as output size times world size"):
+        cs.ccl_sim_reduce_scatter(fake(n, 1003, 8), fake(n, 250, 8, base=BASE * 3), 1003, 250, dtype="int64")
+    with pytest.raises(TypeError):
+        cs.ccl_sim_all_gather(fake(n, 10, 4), fake(n, 41, 4, base=BASE * 3), 10, 41, dtype="float32")
+
+
+def test_argument_validation(cs):
+    n, m = 4, 1000
+    s, r = fake(n, m, 4), fake(n, m, 4, base=BASE * 3)
+    ar = cs.ccl_sim_allreduce
+    assert code_of(ar, s, r, m, dtype="float32", op=9) == cs.INVALID_ARGUMENT
+    assert code_of(ar, s, r, m, dtype=7) == cs.INVALID_ARGUMENT
+    assert code_of(ar, s, r, m, dtype="float32", schedule=5) == cs.INVALID_ARGUMENT
+    assert code_of(ar, [], [], m, dtype="float32") == cs.INVALID_ARGUMENT
+    big = fake(1025, 1, 4)
+    assert code_of(ar, big, fake(1025, 1, 4, base=BASE * 9), 1, dtype="float32") == cs.INVALID_ARGUMENT
+    # null and misaligned pointers
+    assert code_of(ar, [s[0], 0, s[2], s[3]], r, m, dtype="float32") == cs.INVALID_ARGUMENT
+    assert code_of(ar, [s[0] + 2, s[1], s[2], s[3]], r, m, dtype="float32") == cs.INVALID_ARGUMENT
+    assert "aligned" in cs.ccl_sim_last_error()
+    # overlapping outputs
+    r_bad = [r[0], r[0] + 400, r[2], r[3]]
+    assert code_of(ar, s, r_bad, m, dtype="float32") == cs.INVALID_ARGUMENT
+    assert "overlap" in cs.ccl_sim_last_error()
+    # input of one rank overlapping another rank's output
+    s_bad = [r[1], s[1], s[2], s[3]]
+    assert code_of(ar, s_bad, r, m, dtype="float32") == cs.INVALID_ARGUMENT
+    # ring without a workspace
+    assert code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise") == cs.INSUFFICIENT_WORKSPACE
+    need = cs.ccl_sim_workspace_size("allreduce", n, m, "float32", "ring_stepwise")
+    ws = (BASE * 7, need - 1)
+    assert code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise", workspace=ws) == \
+        cs.INSUFFICIENT_WORKSPACE
+    # workspace overlapping a buffer
+    ws_bad = (r[2], need)
+    assert code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise", workspace=ws_bad) == \
+        cs.INVALID_ARGUMENT
+    # misaligned workspace
+    assert code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise", workspace=(BASE * 7 + 64, need)) == \
+        cs.INVALID_ARGUMENT
+    # pad: padded smaller than count
+    assert code_of(cs.ccl_sim_pad_identity, s, r, 10, 9, "max", dtype="float32") == cs.INVALID_ARGUMENT
+
+
+def test_count_zero_is_a_noop_even_with_null_pointers(cs):
+    cs.ccl_sim_allreduce([0] * 4, [0] * 4, 0, dtype="float32")
+    cs.ccl_sim_reduce_scatter([0] * 4, [0] * 4, 0, 0, dtype="int32")
+    cs.ccl_sim_all_gather([0] * 4, [0] * 4, 5, 0, dtype="int32")
+    cs.ccl_sim_pad_identity([0] * 4, [0] * 4, 0, 0, "sum", dtype="int32")
+
+
+def test_in_place_forms_pass_validation_overlap(cs):
+    """The in-place forms are accepted by the overlap check (the call then
+    fails only at the first HIP call when no GPU is present)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check")
+    n, q, es = 4, 256, 4
+    s = fake(n, n * q, es)
+    ok_codes = (0, cs.HIP_ERROR)
+    assert code_of(cs.ccl_sim_allreduce, s, s, n * q, dtype="float32") in ok_codes
+    r = [s[i] + i * q * es for i in range(n)]
+    assert code_of(cs.ccl_sim_reduce_scatter, s, r, n * q, q, dtype="float32") in ok_codes
+    out = fake(n, n * q, es, base=BASE * 5)
+    ins = [out[i] + i * q * es for i in range(n)]
+    assert code_of(cs.ccl_sim_all_gather, ins, out, q, n * q, dtype="float32") in ok_codes
+    # shifted by one shard is not an in-place form
+    r_bad = [s[i] + ((i + 1) % n) * q * es for i in range(n)]
+    assert code_of(cs.ccl_sim_reduce_scatter, s, r_bad, n * q, q, dtype="float32") == cs.INVALID_ARGUMENT
+
+
+def test_workspace_sizes(cs):
+    ws = cs.ccl_sim_workspace_size
+    assert ws("allreduce", 8, 1 << 20, "float32", "direct") == 0
+    assert ws("reduce_scatter", 8, 1 << 20, "float32", "direct") == 0
+    # ring partials: 2 generations x N x q accumulators
+    assert ws("allreduce", 8, 1 << 20, "float32", "ring_stepwise") == 2 * 8 * (1 << 17) * 4
+    assert ws("allreduce", 8, 1 << 20, "bfloat16", "ring_stepwise") == 2 * 8 * (1 << 17) * 4
+    assert ws("allreduce", 2, 1000, "float32", "ring_stepwise") == 0
+    assert ws("all_gather", 8, 1000, "float32", "ring_stepwise") == 0
+    assert ws("all_gather", 8, 1000, "float32", "ring_persistent") == 256
+    # more than 64 ranks: two pointer tables
+    assert ws("allreduce", 256, 1 << 22, "float32", "direct") == 2 * 2048
+    assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == 256 + 4096 + 2 * (1 << 22) * 4
+    assert ws("allreduce", 1, 100, "float32", "ring_persistent") == 0
+    assert ws("allreduce", 0, 100, "float32", "direct") == ctypes.c_size_t(-1).value
+
+
+def test_algorithmic_bytes(cs):
+    ab = cs.ccl_sim_algorithmic_bytes
+    n, m = 8, 1 << 28
+    assert ab("reduce_scatter", n, m, "float32", "direct") == (n + 1) * m * 4
+    assert ab("all_gather", n, m, "float32", "direct") == (n + 1) * m * 4
+    assert ab("allreduce", n, m, "float32", "direct") == 2 * n * m * 4
+    assert ab("reduce_scatter", n, m, "float32", "ring_stepwise") == 3 * (n - 1) * m * 4
+    assert ab("all_gather", n, m, "float32", "ring_persistent") == 2 * n * m * 4
+    assert ab("allreduce", n, m, "float32", "ring_stepwise") == 5 * (n - 1) * m * 4
+    assert ab("allreduce", 256, 1 << 22, "float32", "ring_stepwise") == 21_390_950_400
+    # bf16 with fp32 partials: first step 2+2+4, middle 4+2+4, last 4+2+2 bytes per position
+    n2, m2 = 256, 6_553_600
+    assert ab("reduce_scatter", n2, m2, "bfloat16", "ring_stepwise") == (8 + 10 * (n2 - 3) + 8) * m2
+    assert ab("allreduce", 1, 10, "int64", "ring_stepwise") == 2 * 10 * 8
+
+
+def test_launch_counts_follow_the_step_counts(cs, golden):
+    g = golden("step_counts.json")
+    lc = cs.ccl_sim_launch_count
+    for n, steps in g["allreduce_steps"].items():
+        assert lc("allreduce", int(n), 100, "ring_stepwise") == steps
+    assert lc("reduce_scatter", 4, 100, "ring_stepwise") == g["phase_steps_n4"]
+    assert lc("all_gather", 4, 100, "ring_stepwise", in_place=True) == g["phase_steps_n4"]
+    assert lc("all_gather", 4, 100, "ring_stepwise") == 4
+    assert lc("allreduce", 8, 100, "direct") == 1
+    assert lc("allreduce", 8, 100, "ring_persistent") == 1
+    assert lc("allreduce", 8, 0, "ring_stepwise") == 0
+
+
+def test_ring_routing_matches_the_n4_table(cs, golden):
+    g = golden("ring_n4_routing.json")
+    n = g["nranks"]
+    for t, row in enumerate(g["reduce_scatter_send"]):
+        assert [cs.ccl_sim_ring_route(n, 0, t, r)[0] for r in range(n)] == row
+        assert [cs.ccl_sim_ring_route(n, 0, t, (r + 1) % n)[1] for r in range(n)] == row
+    assert [cs.ccl_sim_ring_owner(n, r) for r in range(n)] == g["owner_after_reduce_scatter"]
+    for t, row in enumerate(g["all_gather_send"]):
+        assert [cs.ccl_sim_ring_route(n, 1, t, r)[0] for r in range(n)] == row
+    # stand-alone AllGather: rank r starts with shard r and first receives r-1
+    assert [cs.ccl_sim_ring_route(n, 2, 0, r)[1] for r in range(n)] == [3, 0, 1, 2]
+    assert cs.ccl_sim_ring_owner(4, 4) == -1
+    with pytest.raises(Exception):
+        cs.ccl_sim_ring_route(4, 0, 3, 0)
+
+
+def test_result_strings(cs):
+    assert cs.ccl_sim_result_string(0) == "success"
+    assert cs.ccl_sim_result_string(5) == "capacity mismatch"

@@ -1,0 +1,366 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Integer results and every copy are compared bit for bit.  Floating results
+are compared bit for bit against the oracle run in the same combining order
+(ascending ranks for the direct schedule, the ring's order for the ring
+schedules), and also held to the tolerance against the float64 sum:
+max normalised error <= 1e-5·N for float32 and <= 1e-2 for bf16 with float32
+accumulation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from oracle import collectives as C
+from oracle import reduction as R
+from oracle import ring as G
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("int32", "int64", "float32", "bfloat16")
+OPS = ("sum", "prod", "max", "min")
+
+
+@pytest.fixture(scope="module")
+def cs():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from collective_reduction_amd import ccl_sim
+    return ccl_sim
+
+
+def oracle_rs(xs, op, dtype, q, schedule):
+    if schedule == "direct":
+        return C.reduce_scatter(xs, op, dtype, q)
+    return G.ring_reduce_scatter(xs, op, dtype, q)
+
+
+def oracle_ar(xs, op, dtype, schedule):
+    if schedule == "direct":
+        return C.direct_allreduce(xs, op, dtype)
+    return G.ring_allreduce(xs, op, dtype)
+
+
+def assert_all_same(outs, want, what):
+    for r, y in enumerate(outs):
+        assert U.same_bits(y, want), f"{what}: rank {r} differs from the oracle"
+
+
+# ---------------------------------------------------------------------------
+# The four-rank, 20-element int64 worked example, every schedule.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_worked_example(cs, golden, schedule):
+    g = golden("worked_example_4x20_int64.json")
+    n, m = g["nranks"], g["count"]
+    xs = [np.array([100 * r + i for i in range(m)], dtype=np.int64) for r in range(n)]
+    shards = U.run_rs(cs, xs, g["shard_len"], "sum", "int64", schedule)
+    assert [s.tolist() for s in shards] == g["shards"]
+    for y in U.run_ag(cs, shards, m, "int64", schedule):
+        assert y.tolist() == g["allreduce"]
+    for y in U.run_ar(cs, xs, "sum", "int64", schedule):
+        assert y.tolist() == g["allreduce"]
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_negative_transforms_differ_on_gpu_outputs(cs, golden, schedule):
+    """RS(MAX)+AG and the rolled shard orders differ from AR(SUM) everywhere."""
+    g = golden("worked_example_4x20_int64.json")
+    n, m = g["nranks"], g["count"]
+    xs = [np.array([100 * r + i for i in range(m)], dtype=np.int64) for r in range(n)]
+    direct = U.run_ar(cs, xs, "sum", "int64", schedule)[0]
+    max_gathered = U.run_ag(cs, U.run_rs(cs, xs, 5, "max", "int64", schedule), m, "int64", schedule)[0]
+    assert np.all(max_gathered != direct)
+    for shifts in (1, -1):
+        assert np.all(C.roll_shards(U.run_ag(cs, U.run_rs(cs, xs, 5, "sum", "int64", schedule), m, "int64",
+                                             schedule)[0], n, shifts) != direct)
+
+
+# ---------------------------------------------------------------------------
+# Small matrix: every dtype, op and schedule; sizes that span several tiles
+# with a ragged tail; 1 <= N <= 8.
+# ---------------------------------------------------------------------------
+
+SIZES = [(1, 5003), (2, 1), (3, 5003), (5, 3), (8, 5003), (8, 4096)]
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_reduce_scatter_matrix(cs, dtype, op, schedule):
+    for n, q in SIZES:
+        xs = U.random_inputs(n, n * q, dtype, seed=1000 + n * 7 + q, op=op)
+        got = U.run_rs(cs, xs, q, op, dtype, schedule)
+        want = oracle_rs(xs, op, dtype, q, schedule)
+        for r in range(n):
+            assert U.same_bits(got[r], want[r]), (n, q, r)
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_all_gather_matrix(cs, dtype, schedule):
+    for n, q in SIZES:
+        shards = U.random_inputs(n, q, dtype, seed=2000 + n + q)
+        for recvcount in {n * q, max(n * q - (n - 1), 0), max(n * q - q - 1, 0)}:
+            got = U.run_ag(cs, shards, recvcount, dtype, schedule)
+            want = C.all_gather(shards, recvcount)
+            assert_all_same(got, want[0], f"AG n={n} q={q} recv={recvcount}")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_matrix(cs, dtype, op, schedule):
+    for n, q in SIZES:
+        for m in {n * q, max(n * q - (n - 1), 1), n * q + 1}:
+            xs = U.random_inputs(n, m, dtype, seed=3000 + n + m, op=op)
+            got = U.run_ar(cs, xs, op, dtype, schedule)
+            want = oracle_ar(xs, op, dtype, schedule)
+            assert_all_same(got, want[0], f"AR n={n} m={m}")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_allreduce_tiny_and_empty(cs, schedule):
+    for n, m in [(8, 1), (8, 7), (4, 3), (1, 1)]:
+        xs = U.random_inputs(n, m, "float32", seed=n * 31 + m)
+        got = U.run_ar(cs, xs, "sum", "float32", schedule)
+        assert_all_same(got, oracle_ar(xs, "sum", "float32", schedule)[0], f"n={n} m={m}")
+    # count 0 enqueues nothing and touches nothing
+    z = [U.empty(4, "float32") for _ in range(3)]
+    cs.ccl_sim_allreduce(z, z, 0, schedule=schedule, dtype="float32")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_rs_then_ag_equals_allreduce_bitwise(cs, schedule):
+    """The same order gives the same bits: RS+AG of one schedule equals that
+    schedule's AllReduce, and all N outputs are identical."""
+    n, q = 8, 3001
+    xs = U.random_inputs(n, n * q, "float32", seed=5)
+    ar = U.run_ar(cs, xs, "sum", "float32", schedule)
+    rs_ag = U.run_ag(cs, U.run_rs(cs, xs, q, "sum", "float32", schedule), n * q, "float32", schedule)
+    for r in range(n):
+        assert U.same_bits(ar[r], ar[0])
+        assert U.same_bits(rs_ag[r], ar[0])
+
+
+# ---------------------------------------------------------------------------
+# Layout variants: misaligned bases, in-place forms, more than 64 ranks.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_misaligned_base_addresses(cs, dtype, schedule):
+    n, q = 5, 2049
+    xs = U.random_inputs(n, n * q, dtype, seed=77)
+    got = U.run_rs(cs, xs, q, "sum", dtype, schedule, offset=1)
+    want = oracle_rs(xs, "sum", dtype, q, schedule)
+    for r in range(n):
+        assert U.same_bits(got[r], want[r])
+    got = U.run_ag(cs, want, n * q - 2, dtype, schedule, offset=1)
+    assert_all_same(got, C.all_gather(want, n * q - 2)[0], "AG offset")
+    got = U.run_ar(cs, xs, "max", dtype, schedule, offset=1)
+    assert_all_same(got, oracle_ar(xs, "max", dtype, schedule)[0], "AR offset")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_in_place_forms(cs, schedule):
+    n, q = 6, 1027
+    for dtype in ("float32", "bfloat16", "int64"):
+        xs = U.random_inputs(n, n * q, dtype, seed=9)
+        got = U.run_ar(cs, xs, "sum", dtype, schedule, in_place=True)
+        assert_all_same(got, oracle_ar(xs, "sum", dtype, schedule)[0], f"AR in place {dtype}")
+        got = U.run_rs(cs, xs, q, "sum", dtype, schedule, in_place=True)
+        want = oracle_rs(xs, "sum", dtype, q, schedule)
+        for r in range(n):
+            assert U.same_bits(got[r], want[r])
+        got = U.run_ag(cs, want, n * q - 3, dtype, schedule, in_place=True)
+        assert_all_same(got, C.all_gather(want, n * q - 3)[0], f"AG in place {dtype}")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_more_ranks_than_fit_in_kernel_arguments(cs, schedule):
+    for n, q in [(65, 3), (100, 37), (256, 9)]:
+        xs = U.random_inputs(n, n * q, "float32", seed=n)
+        got = U.run_rs(cs, xs, q, "sum", "float32", schedule)
+        want = oracle_rs(xs, "sum", "float32", q, schedule)
+        for r in range(n):
+            assert U.same_bits(got[r], want[r]), (n, r)
+        m = n * q - n // 2
+        got = U.run_ar(cs, [x[:m] for x in xs], "sum", "float32", schedule)
+        assert_all_same(got, oracle_ar([x[:m] for x in xs], "sum", "float32", schedule)[0], f"AR n={n}")
+        got = U.run_ag(cs, want, m, "float32", schedule)
+        assert_all_same(got, C.all_gather(want, m)[0], f"AG n={n}")
+
+
+# ---------------------------------------------------------------------------
+# Identity padding, and where the pad value is observable.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("dtype,op,ident_bits", [("float32", "max", 0xFF800000), ("int32", "sum", 0),
+                                                 ("bfloat16", "min", 0x7F80), ("int64", "prod", 1)])
+def test_pad_rs_ag_trim(cs, schedule, dtype, op, ident_bits):
+    n, m = 8, 10_003
+    q = C.shard_count(m, n)
+    xs = U.random_inputs(n, m, dtype, seed=41, op=op)
+    src = U.bufs_from(xs, dtype)
+    padded = [U.empty(n * q, dtype) for _ in range(n)]
+    cs.ccl_sim_pad_identity(src, padded, m, n * q, op, dtype=dtype)
+    want_pad = C.pad_identity(xs, op, dtype, n * q)
+    for r in range(n):
+        assert U.same_bits(U.to_host(padded[r], dtype), want_pad[r])
+    shards = [U.empty(q, dtype) for _ in range(n)]
+    ws = cs.Workspace("reduce_scatter", n, n * q, dtype, schedule)
+    cs.ccl_sim_reduce_scatter(padded, shards, n * q, q, op=op, schedule=schedule, workspace=ws, dtype=dtype)
+    torch.cuda.synchronize()
+    got_shards = [U.to_host(z, dtype) for z in shards]
+    want_shards = oracle_rs(want_pad, op, dtype, q, schedule)
+    for r in range(n):
+        assert U.same_bits(got_shards[r], want_shards[r])
+    tail = got_shards[-1][m - (n - 1) * q:]
+    assert tail.size == n * q - m
+    view = {"float32": np.uint32, "bfloat16": np.uint16}.get(dtype)
+    assert np.all((tail.view(view) if view else tail) == ident_bits)
+    out = U.run_ag(cs, got_shards, m, dtype, schedule)
+    if schedule == "direct":
+        assert_all_same(out, C.allreduce_via_rs_ag(xs, op, dtype)[0], "pad+RS+AG")
+    assert_all_same(out, oracle_ar(xs, op, dtype, schedule)[0], "pad+RS+AG vs AR")
+
+
+def test_pad_in_place_fills_only_the_tail(cs):
+    n, m, p = 3, 1000, 1024
+    xs = U.random_inputs(n, p, "float32", seed=3)
+    bufs = U.bufs_from(xs, "float32")
+    cs.ccl_sim_pad_identity(bufs, bufs, m, p, "max", dtype="float32")
+    for r in range(n):
+        h = U.to_host(bufs[r], "float32")
+        assert U.same_bits(h[:m], xs[r][:m])
+        assert np.all(np.isneginf(h[m:]))
+
+
+# ---------------------------------------------------------------------------
+# The configurations at full size.
+# ---------------------------------------------------------------------------
+
+def _tolerance_ok(y, xs, dtype, n):
+    err = R.normalized_sum_error(y, xs, dtype)
+    bound = 1e-5 * n if dtype == "float32" else 1e-2
+    assert err <= bound, (err, bound)
+    return err
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_uniform_8x1m_fp32_full(cs, schedule):
+    """N=8, M=2^20 uniform[-1,1) float32 SUM: RS-only and RS+AG, every element."""
+    from collective_reduction_amd import inputs as I
+    s = I.spec("uniform_8x1048576_fp32")
+    n, m = s["nranks"], s["count"]
+    xs = list(I.all_buffers(s))
+    q = m // n
+    shards = U.run_rs(cs, xs, q, "sum", "float32", schedule)
+    want = oracle_rs(xs, "sum", "float32", q, schedule)
+    for r in range(n):
+        assert U.same_bits(shards[r], want[r])
+    full = U.run_ag(cs, shards, m, "float32", schedule)
+    assert_all_same(full, np.concatenate(want), "RS+AG")
+    _tolerance_ok(full[0], xs, "float32", n)
+    ar = U.run_ar(cs, xs, "sum", "float32", schedule)
+    assert_all_same(ar, np.concatenate(want), "AR")
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_nondivisible_8x1000003_full(cs, schedule):
+    """N=8, M=1,000,003 (q=125,001, 5 pad elements): float32 normal MAX with
+    -inf padding and int32 SUM with zero padding, every element."""
+    from collective_reduction_amd import inputs as I
+    for name, op in (("normal_8x1000003_fp32", "max"), ("intuniform_8x1000003_int32", "sum")):
+        s = I.spec(name)
+        n, m, dtype = s["nranks"], s["count"], s["dtype"]
+        xs = list(I.all_buffers(s))
+        q = C.shard_count(m, n)
+        assert q == 125_001
+        src = U.bufs_from(xs, dtype)
+        padded = [U.empty(n * q, dtype) for _ in range(n)]
+        cs.ccl_sim_pad_identity(src, padded, m, n * q, op, dtype=dtype)
+        shards = [U.empty(q, dtype) for _ in range(n)]
+        ws = cs.Workspace("reduce_scatter", n, n * q, dtype, schedule)
+        cs.ccl_sim_reduce_scatter(padded, shards, n * q, q, op=op, schedule=schedule, workspace=ws, dtype=dtype)
+        torch.cuda.synchronize()
+        got = [U.to_host(z, dtype) for z in shards]
+        want = oracle_rs(C.pad_identity(xs, op, dtype, n * q), op, dtype, q, schedule)
+        for r in range(n):
+            assert U.same_bits(got[r], want[r]), (name, r)
+        tail = got[-1][m - (n - 1) * q:]
+        assert tail.size == 5
+        if dtype == "float32":
+            assert np.all(tail.view(np.uint32) == 0xFF800000)
+        else:
+            assert np.all(tail == 0)
+        out = U.run_ag(cs, got, m, dtype, schedule)
+        assert_all_same(out, np.concatenate(want)[:m], name)
+        ar = U.run_ar(cs, xs, op, dtype, schedule)
+        assert_all_same(ar, np.concatenate(want)[:m], name + " AR")
+
+
+def _sampled_check(cs, s, schedule, op, k, seed, coll="allreduce"):
+    """Run the collective at full size; compare sampled positions bit for bit
+    with the oracle folded in the schedule's order, check every rank agrees
+    there, and check the float tolerance on the samples."""
+    from collective_reduction_amd import inputs as I
+    n, m, dtype = s["nranks"], s["count"], s["dtype"]
+    q = C.shard_count(m, n)
+    send = U.upload_workload(s)
+    ws = cs.Workspace("allreduce" if coll == "allreduce" else "reduce_scatter", n, m, dtype, schedule)
+    pos = U.sample_positions(m, q, k, seed)
+    if coll == "allreduce":
+        recv = [U.empty(m, dtype) for _ in range(n)]
+        cs.ccl_sim_allreduce(send, recv, m, op=op, schedule=schedule, workspace=ws, dtype=dtype)
+    else:
+        shards = [U.empty(q, dtype) for _ in range(n)]
+        cs.ccl_sim_reduce_scatter(send, shards, m, q, op=op, schedule=schedule, workspace=ws, dtype=dtype)
+        del send
+        recv = [U.empty(m, dtype) for _ in range(n)]
+        ws2 = cs.Workspace("all_gather", n, m, dtype, schedule)
+        cs.ccl_sim_all_gather(shards, recv, q, m, schedule=schedule, workspace=ws2, dtype=dtype)
+    torch.cuda.synchronize()
+    cols = I.gather_positions(s, pos)
+    xs = [cols[r] for r in range(n)]
+    want = np.empty(pos.size, dtype=U.NP[dtype])
+    if schedule == "direct":
+        want[:] = R.narrow(C.fold(xs, op, dtype, list(range(n))), dtype)
+    else:
+        chunks = pos // q
+        for c in np.unique(chunks):
+            sel = np.nonzero(chunks == c)[0]
+            want[sel] = R.narrow(C.fold([x[sel] for x in xs], op, dtype, G.chunk_order(n, int(c))), dtype)
+    for r in range(0, n, max(1, n // 8)):
+        got = U.pick(recv[r], pos, dtype)
+        assert U.same_bits(got, want), f"rank {r}"
+    if dtype in ("float32", "bfloat16") and op == "sum":
+        _tolerance_ok(want, xs, dtype, n)
+    del recv
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_gradient_256x4m_fp32_sampled(cs, schedule):
+    """N=256 ranks, M=2^22 normal(0,1e-3) float32 SUM; the ring runs 510 steps."""
+    from collective_reduction_amd import inputs as I
+    _sampled_check(cs, I.spec("normal_256x4194304_fp32"), schedule, "sum", 4096, 11)
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_gradient_256x6553600_bf16_sampled(cs, schedule):
+    """The 6,553,600-element bf16 bucket over 256 ranks, float32 accumulation."""
+    from collective_reduction_amd import inputs as I
+    _sampled_check(cs, I.spec("normal_256x6553600_bf16"), schedule, "sum", 4096, 12)
+
+
+@pytest.mark.parametrize("schedule", ["direct", "ring_stepwise"])
+def test_uniform_8x256m_fp32_rs_ag_sampled(cs, schedule):
+    """N=8, M=2^28 (1 GiB per rank) float32: RS then AG at full size."""
+    from collective_reduction_amd import inputs as I
+    _sampled_check(cs, I.spec("uniform_8x268435456_fp32"), schedule, "sum", 1 << 15, 13, coll="rs_ag")
