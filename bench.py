@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle work for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--counters-pass", action="store_true",
+                   help="run one RS, one AG and one plain copy of known size, for rocprofv3 --pmc")
     return p.parse_args()
 
 
@@ -166,6 +168,10 @@ def main():
     recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
     torch.cuda.synchronize()
 
+    if args.counters_pass:
+        counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype)
+        return
+
     bytes_rs = cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct")
     bytes_ag = cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")
     bytes_step = bytes_rs + bytes_ag
@@ -252,6 +258,23 @@ def main():
         "kernel_source_digest": kernel_source_digest(),
     }
     print(json.dumps(out), flush=True)
+
+
+def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
+    """One launch of each kernel the bench times, for hardware counters: the
+    ReduceScatter, the AllGather, and ccl_sim_pad_identity with nothing to
+    pad, a plain copy of N·M elements (reads and writes N·M·s bytes) that
+    calibrates FETCH_SIZE / WRITE_SIZE against a known byte count."""
+    cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", stream=stream)
+    cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", stream=stream)
+    cs.ccl_sim_pad_identity(send, recv, m, m, "sum", stream=stream)
+    torch.cuda.synchronize()
+    es = send[0].element_size()
+    print(json.dumps({"counters_pass": True, "rs_bytes": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype,
+                                                                                      "direct"),
+                      "ag_bytes": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct"),
+                      "copy_read_bytes": n * m * es, "copy_write_bytes": n * m * es,
+                      "kernel_source_digest": kernel_source_digest()}), flush=True)
 
 
 def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):

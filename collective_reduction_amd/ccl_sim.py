@@ -17,7 +17,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libccl_sim.so")
+# CCL_SIM_LIBRARY may name another build of the same library (a debug or
+# tuning variant); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("CCL_SIM_LIBRARY") or os.path.join(_HERE, "libccl_sim.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -86,6 +87,28 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
 }
 
 std::atomic<int> g_cus[64];
+
+// Environment knobs, read once.
+//   CCL_SIM_DEBUG=1                      log each launch plan to stderr; after a
+//                                        persistent ring, wait for it and report a
+//                                        barrier that hit its poll limit
+//   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU
+//   CCL_SIM_SPIN_LIMIT=n                 persistent ring barrier poll limit
+struct Env {
+  bool debug = false;
+  int per_cu = 0;
+  unsigned spin_limit = 0;
+  Env() {
+    if (const char* v = std::getenv("CCL_SIM_DEBUG")) debug = std::atoi(v) != 0;
+    if (const char* v = std::getenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU")) per_cu = std::atoi(v);
+    if (const char* v = std::getenv("CCL_SIM_SPIN_LIMIT")) spin_limit = static_cast<unsigned>(std::strtoul(v, nullptr, 10));
+  }
+};
+
+const Env& env() {
+  static const Env e;
+  return e;
+}
 
 hipError_t device_cus(int* cus) {
   int dev = 0;
@@ -248,6 +271,9 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (lay.partial != SIZE_MAX) c.partial = ws + lay.partial;
   if (lay.ctrl != SIZE_MAX) c.ctrl = reinterpret_cast<unsigned*>(ws + lay.ctrl);
   c.stream = stream;
+  c.persistent_per_cu = env().per_cu;
+  c.spin_limit = env().spin_limit;
+  c.log_plan = env().debug;
 
   hipError_t e = device_cus(&c.num_cus);
   if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "device query failed: %s", hipGetErrorString(e));
@@ -273,11 +299,32 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     e = run_ring_stepwise(c);
   } else {
     bool unsupported = false;
-    e = run_ring_persistent(c, &unsupported);
+    PersistentPlan plan;
+    e = run_ring_persistent(c, &unsupported, &plan);
     if (e == hipSuccess && unsupported)
       return fail(CCL_SIM_UNSUPPORTED, "no co-resident grid for the persistent ring kernel on this device");
+    if (c.log_plan)
+      std::fprintf(stderr,
+                   "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu "
+                   "tiles/step=%llu\n",
+                   coll, nranks, static_cast<unsigned long long>(q), c.num_cus, plan.occupancy_per_cu, plan.per_cu,
+                   static_cast<unsigned long long>(plan.grid), static_cast<unsigned long long>(plan.tiles_per_step));
+    if (e == hipSuccess && c.log_plan) {
+      // Debug check of the barrier's watchdog: wait for the kernel and read
+      // the abort word it raises when a barrier runs into the poll limit.
+      unsigned abort_word = 0;
+      e = hipStreamSynchronize(stream);
+      if (e == hipSuccess)
+        e = hipMemcpy(&abort_word, c.ctrl + kCtrlAbort, sizeof(abort_word), hipMemcpyDeviceToHost);
+      if (e == hipSuccess && abort_word != 0)
+        return fail(CCL_SIM_HIP_ERROR, "persistent ring barrier reached its poll limit; the results are incomplete");
+    }
   }
   if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));
+  if (c.log_plan)
+    std::fprintf(stderr, "[ccl_sim] coll=%d sched=%d N=%d M=%llu q=%llu dtype=%d op=%d in_place=%d tables=%d\n", coll,
+                 sched, nranks, static_cast<unsigned long long>(m), static_cast<unsigned long long>(q), dtype, op,
+                 int(c.in_place), int(nranks > kInlineRanks));
   return CCL_SIM_SUCCESS;
 }
 

@@ -11,16 +11,15 @@
 
 namespace ccl {
 
-constexpr int kBlock = 256;       // threads per workgroup: 4 wave64s
+#ifndef CCL_SIM_BLOCK
+#define CCL_SIM_BLOCK 256
+#endif
+constexpr int kBlock = CCL_SIM_BLOCK;  // threads per workgroup (256 = 4 wave64s)
 constexpr int kInlineRanks = 64;  // rank pointers passed in the kernel arguments
 
-#ifndef CCL_SIM_UNROLL
-#define CCL_SIM_UNROLL 2          // 16-byte vectors per lane per tile
-#endif
 #ifndef CCL_SIM_RANK_BATCH
 #define CCL_SIM_RANK_BATCH 8      // rank loads issued before they are combined
 #endif
-constexpr int kUnroll = CCL_SIM_UNROLL;
 constexpr int kRankBatch = CCL_SIM_RANK_BATCH;
 
 // The reduction operators of [PRIMS] §二.1.

@@ -25,6 +25,19 @@ struct Call {
   unsigned* ctrl = nullptr;// persistent ring: barrier counter and abort flag
   hipStream_t stream = nullptr;
   int num_cus = 0;
+  // Persistent ring: workgroups per compute unit (0 = the default), the
+  // barrier's poll limit, and whether to log the launch plan to stderr.
+  int persistent_per_cu = 0;
+  unsigned spin_limit = 0;
+  bool log_plan = false;
+};
+
+// Grid actually launched by run_ring_persistent (for diagnostics).
+struct PersistentPlan {
+  int occupancy_per_cu = 0;
+  int per_cu = 0;
+  uint64_t grid = 0;
+  uint64_t tiles_per_step = 0;
 };
 
 // Control block layout (unsigned words) at the start of the workspace.
@@ -33,7 +46,7 @@ enum CtrlWord : int { kCtrlBarrier = 0, kCtrlAbort = 1, kCtrlWords = 64 };
 hipError_t run_direct(const Call& c);
 hipError_t run_ring_stepwise(const Call& c);
 // Sets *unsupported when no co-resident grid can be formed.
-hipError_t run_ring_persistent(const Call& c, bool* unsupported);
+hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan);
 hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded);
 // Copy `n` host-side pointers into a device table on the stream (kernel
 // arguments carry them; no host-to-device memcpy).

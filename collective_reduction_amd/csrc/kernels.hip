@@ -9,8 +9,8 @@
 //   [WHY-EQ] "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
 //
 // Work decomposition.  Every kernel is a grid-stride loop over tiles of
-// kBlock·V·kUnroll elements (V = 16 / sizeof(element): one 128-bit access
-// per lane per vector).  A tile never crosses a shard (or ring chunk)
+// kBlock·V·U elements (V = 16 / sizeof(element): one 128-bit access per
+// lane per vector, U vectors per lane; U is part of each kernel's Policy).  A tile never crosses a shard (or ring chunk)
 // boundary, so the shard a tile belongs to is one scalar division per tile
 // and the shard-local side of every access keeps the buffer's alignment;
 // the other side (the input of ReduceScatter at r·q + j, the output of
@@ -37,7 +37,40 @@ constexpr int vec_elems() {
   return 16 / static_cast<int>(sizeof(typename T::S));
 }
 
-constexpr uint64_t tile_of(int v) { return uint64_t(kBlock) * uint64_t(v) * kUnroll; }
+// Per-kernel memory policy: U 128-bit vectors per lane per tile, and
+// whether rank-buffer loads / stores carry the nontemporal hint.  Every
+// rank buffer is streamed once per call, so keeping it out of the caches
+// pays where a kernel mostly reads (ReduceScatter, AllReduce, ring steps);
+// the AllGather, which writes N times what it reads, is faster with
+// ordinary accesses.  Each default can be replaced at build time.
+template <int U_, bool NTL_, bool NTS_>
+struct Policy {
+  static constexpr int U = U_;
+  static constexpr bool NTL = NTL_;
+  static constexpr bool NTS = NTS_;
+};
+#ifndef CCL_SIM_RS_POLICY
+#define CCL_SIM_RS_POLICY 4, true, true
+#endif
+#ifndef CCL_SIM_AG_POLICY
+#define CCL_SIM_AG_POLICY 4, false, false
+#endif
+#ifndef CCL_SIM_AR_POLICY
+#define CCL_SIM_AR_POLICY 4, true, true
+#endif
+#ifndef CCL_SIM_RING_POLICY
+#define CCL_SIM_RING_POLICY 4, true, true
+#endif
+using RsPolicy = Policy<CCL_SIM_RS_POLICY>;
+using AgPolicy = Policy<CCL_SIM_AG_POLICY>;
+using ArPolicy = Policy<CCL_SIM_AR_POLICY>;
+using RingPolicy = Policy<CCL_SIM_RING_POLICY>;
+using PadPolicy = Policy<4, false, false>;
+
+template <class P>
+constexpr uint64_t tile_of(int v) {
+  return uint64_t(kBlock) * uint64_t(v) * P::U;
+}
 
 // K elements of E as one vector value, promising only element alignment.
 // gfx950 under the HSA runtime accepts unaligned global accesses, so the
@@ -51,13 +84,21 @@ struct VecOf {
 
 // Accesses go through global-address-space pointers so they compile to
 // global_load / global_store rather than flat accesses.
-template <class E, int K>
+template <class E, int K, bool NT>
 __device__ inline typename VecOf<E, K>::type vload(const E* p) {
-  return *(const CCL_GLOBAL typename VecOf<E, K>::type*)(p);
+  using V = typename VecOf<E, K>::type;
+  if constexpr (NT)
+    return __builtin_nontemporal_load((const CCL_GLOBAL V*)(p));
+  else
+    return *(const CCL_GLOBAL V*)(p);
 }
-template <class E, int K>
+template <class E, int K, bool NT>
 __device__ inline void vstore(E* p, typename VecOf<E, K>::type v) {
-  *(CCL_GLOBAL typename VecOf<E, K>::type*)(p) = v;
+  using V = typename VecOf<E, K>::type;
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, (CCL_GLOBAL V*)(p));
+  else
+    *(CCL_GLOBAL V*)(p) = v;
 }
 template <class E>
 __device__ inline E get1(const E* p) {
@@ -72,64 +113,54 @@ __device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
   return j < len ? static_cast<int>(len - j < static_cast<uint64_t>(v) ? len - j : static_cast<uint64_t>(v)) : 0;
 }
 
-// One lane's kUnroll vectors inside a tile.  FULL: the whole tile lies
-// inside the valid range, so every vector is complete and no lane checks a
-// count; otherwise each vector carries its count of valid elements (0..V)
-// and incomplete ones move element by element.
-template <class T, bool FULL>
+// One lane's P::U vectors inside a tile.  FULL: the whole tile lies inside
+// the valid range, so every vector is complete and no lane checks a count;
+// otherwise each vector carries its count of valid elements (0..V) and
+// incomplete ones move element by element.
+template <class T, class P, bool FULL>
 struct Lane {
   using S = typename T::S;
   using A = typename T::A;
+  static constexpr int U = P::U;
   static constexpr int V = vec_elems<T>();
   using SV = typename VecOf<S, V>::type;
   using AV = typename VecOf<A, V>::type;
-  uint64_t j[kUnroll];
-  int cnt[kUnroll];
+  uint64_t j[U];
+  int cnt[U];
 
   __device__ Lane(uint64_t seg, uint64_t len) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      j[u] = seg * tile_of(V) + uint64_t(u * kBlock + static_cast<int>(threadIdx.x)) * V;
+    for (int u = 0; u < U; ++u) {
+      j[u] = seg * tile_of<P>(V) + uint64_t(u * kBlock + static_cast<int>(threadIdx.x)) * V;
       cnt[u] = FULL ? V : lane_count(j[u], len, V);
     }
   }
   __device__ bool on(int u) const { return FULL || cnt[u] > 0; }
   __device__ bool whole(int u) const { return FULL || cnt[u] == V; }
 
-  __device__ SV load(const S* base, int u) const {
-    if (whole(u)) return vload<S, V>(base + j[u]);
-    SV v = {};
+  template <class E, class EV>
+  __device__ EV load_any(const E* base, int u) const {
+    if (whole(u)) return vload<E, V, P::NTL>(base + j[u]);
+    EV v = {};
 #pragma unroll
     for (int k = 0; k < V; ++k)
       if (k < cnt[u]) v[k] = get1(base + j[u] + k);
     return v;
   }
-  __device__ void store(S* base, int u, SV v) const {
+  template <class E, class EV>
+  __device__ void store_any(E* base, int u, EV v) const {
     if (whole(u)) {
-      vstore<S, V>(base + j[u], v);
+      vstore<E, V, P::NTS>(base + j[u], v);
       return;
     }
 #pragma unroll
     for (int k = 0; k < V; ++k)
-      if (k < cnt[u]) put1(base + j[u] + k, static_cast<S>(v[k]));
+      if (k < cnt[u]) put1(base + j[u] + k, static_cast<E>(v[k]));
   }
-  __device__ AV load_acc(const A* base, int u) const {
-    if (whole(u)) return vload<A, V>(base + j[u]);
-    AV v = {};
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-      if (k < cnt[u]) v[k] = get1(base + j[u] + k);
-    return v;
-  }
-  __device__ void store_acc(A* base, int u, AV v) const {
-    if (whole(u)) {
-      vstore<A, V>(base + j[u], v);
-      return;
-    }
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-      if (k < cnt[u]) put1(base + j[u] + k, static_cast<A>(v[k]));
-  }
+  __device__ SV load(const S* base, int u) const { return load_any<S, SV>(base, u); }
+  __device__ void store(S* base, int u, SV v) const { store_any<S, SV>(base, u, v); }
+  __device__ AV load_acc(const A* base, int u) const { return load_any<A, AV>(base, u); }
+  __device__ void store_acc(A* base, int u, AV v) const { store_any<A, AV>(base, u, v); }
 };
 
 template <class T>
@@ -144,22 +175,23 @@ __device__ inline const typename T::S* in_ptr(const RankPtrs& p, int r) {
 
 // acc[u][k] = x^(0) ⊕ x^(1) ⊕ ... ⊕ x^(N-1) at offset off + j[u] + k, folded
 // strictly in ascending rank order.  Loads of kRankBatch ranks are issued
-// before any of them is combined, so each lane keeps up to
-// kRankBatch·kUnroll 128-bit loads in flight; the order of the combines is
-// still x^(0), x^(1), ... regardless.
-template <class T, int OP, bool FULL>
-__device__ inline void fold_ranks(const RankPtrs& src, int nranks, uint64_t off, const Lane<T, FULL>& ln,
-                                  typename T::A (&acc)[kUnroll][vec_elems<T>()]) {
+// before any of them is combined, so each lane keeps up to kRankBatch·U
+// 128-bit loads in flight; the order of the combines is still x^(0),
+// x^(1), ... regardless.
+template <class T, int OP, class P, bool FULL>
+__device__ inline void fold_ranks(const RankPtrs& src, int nranks, uint64_t off, const Lane<T, P, FULL>& ln,
+                                  typename T::A (&acc)[P::U][vec_elems<T>()]) {
   constexpr int V = vec_elems<T>();
-  using SV = typename Lane<T, FULL>::SV;
+  constexpr int U = P::U;
+  using SV = typename Lane<T, P, FULL>::SV;
   for (int s0 = 0; s0 < nranks; s0 += kRankBatch) {
-    SV buf[kRankBatch][kUnroll];
+    SV buf[kRankBatch][U];
 #pragma unroll
     for (int b = 0; b < kRankBatch; ++b) {
       if (s0 + b < nranks) {
         const typename T::S* p = in_ptr<T>(src, s0 + b) + off;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
           if (ln.on(u)) buf[b][u] = ln.load(p, u);
       }
     }
@@ -167,7 +199,7 @@ __device__ inline void fold_ranks(const RankPtrs& src, int nranks, uint64_t off,
     for (int b = 0; b < kRankBatch; ++b) {
       if (s0 + b < nranks) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int k = 0; k < V; ++k) {
             const typename T::A x = T::widen(buf[b][u][k]);
@@ -178,9 +210,9 @@ __device__ inline void fold_ranks(const RankPtrs& src, int nranks, uint64_t off,
   }
 }
 
-template <class T, bool FULL>
-__device__ inline typename Lane<T, FULL>::SV narrow_vec(const typename T::A (&acc)[vec_elems<T>()]) {
-  typename Lane<T, FULL>::SV v;
+template <class T, class SV>
+__device__ inline SV narrow_vec(const typename T::A (&acc)[vec_elems<T>()]) {
+  SV v;
 #pragma unroll
   for (int k = 0; k < vec_elems<T>(); ++k) v[k] = T::narrow(acc[k]);
   return v;
@@ -203,19 +235,21 @@ struct ShardArgs {
 // write of the shards: (N+1)·M elements of HBM traffic.
 template <class T, int OP, bool FULL>
 __device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
+  using P = RsPolicy;
+  using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
-  const Lane<T, FULL> ln(seg, a.q);
-  typename T::A acc[kUnroll][V];
-  fold_ranks<T, OP, FULL>(a.send, a.nranks, uint64_t(r) * a.q, ln, acc);
+  const L ln(seg, a.q);
+  typename T::A acc[P::U][V];
+  fold_ranks<T, OP, P, FULL>(a.send, a.nranks, uint64_t(r) * a.q, ln, acc);
   typename T::S* out = out_ptr<T>(a.recv, r);
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
-    if (ln.on(u)) ln.store(out, u, narrow_vec<T, FULL>(acc[u]));
+  for (int u = 0; u < P::U; ++u)
+    if (ln.on(u)) ln.store(out, u, narrow_vec<T, typename L::SV>(acc[u]));
 }
 
 template <class T, int OP>
 __global__ __launch_bounds__(kBlock) void rs_direct_kernel(ShardArgs a) {
-  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  constexpr uint64_t kTile = tile_of<RsPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int r = static_cast<int>(tile / a.tiles_per_shard);
     const uint64_t seg = tile - uint64_t(r) * a.tiles_per_shard;
@@ -229,36 +263,140 @@ __global__ __launch_bounds__(kBlock) void rs_direct_kernel(ShardArgs a) {
 // AllGather: recv[r][s·q + j] = send[s][j] for every r, positions below
 // `limit` only ([DECOMP] §数学证明 AllGather, trim of §Contract 实验四).
 // Each shard vector is read once into registers and stored N times.
+#ifndef CCL_SIM_AG_ROTATE
+#define CCL_SIM_AG_ROTATE 0
+#endif
+
 template <class T, bool FULL>
-__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
-  using SV = typename Lane<T, FULL>::SV;
-  const Lane<T, FULL> ln(seg, len);
+__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len, uint64_t tile) {
+  using P = AgPolicy;
+  using L = Lane<T, P, FULL>;
+  const L ln(seg, len);
   const uint64_t base = uint64_t(s) * a.q;
   const typename T::S* src = in_ptr<T>(a.send, s);
-  SV v[kUnroll];
+  typename L::SV v[P::U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
+  for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) v[u] = ln.load(src, u);
-  for (int r = 0; r < a.nranks; ++r) {
+  // With CCL_SIM_AG_ROTATE each tile starts its N stores at a different
+  // rank, spreading concurrent writes over all output buffers.
+  const int first = CCL_SIM_AG_ROTATE ? static_cast<int>(tile % uint64_t(a.nranks)) : 0;
+  for (int i = 0; i < a.nranks; ++i) {
+    int r = first + i;
+    if (r >= a.nranks) r -= a.nranks;
     typename T::S* dst = out_ptr<T>(a.recv, r) + base;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) ln.store(dst, u, v[u]);
   }
 }
 
 template <class T>
 __global__ __launch_bounds__(kBlock) void ag_direct_kernel(ShardArgs a) {
-  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int s = static_cast<int>(tile / a.tiles_per_shard);
     const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
     const uint64_t base = uint64_t(s) * a.q;
     const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
     if ((seg + 1) * kTile <= len)
-      ag_tile<T, true>(a, s, seg, len);
+      ag_tile<T, true>(a, s, seg, len, tile);
     else
-      ag_tile<T, false>(a, s, seg, len);
+      ag_tile<T, false>(a, s, seg, len, tile);
+  }
+}
+
+// AllGather, XCD-aware variant: one work item copies one shard tile to ONE
+// output rank.  Item i runs on XCD i mod 8 (workgroups are dealt to the
+// eight XCDs round-robin and the grid is a multiple of 8), and the N items
+// of a shard tile are numbered 8 apart, so they land on the same XCD at
+// about the same time: the shard tile comes from HBM once and from that
+// XCD's L2 for the other N-1 copies, while every workgroup streams a single
+// output buffer.
+template <class T>
+__global__ __launch_bounds__(kBlock) void ag_xcd_kernel(ShardArgs a, uint64_t nitems) {
+  constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
+  const uint64_t n = uint64_t(a.nranks);
+  for (uint64_t i = blockIdx.x; i < nitems; i += gridDim.x) {
+    const uint64_t l = i / 8;
+    const uint64_t st = (l / n) * 8 + (i % 8);  // shard tile
+    const int r = static_cast<int>(l % n);      // output rank
+    if (st >= a.ntiles) continue;
+    const int s = static_cast<int>(st / a.tiles_per_shard);
+    const uint64_t seg = st - uint64_t(s) * a.tiles_per_shard;
+    const uint64_t base = uint64_t(s) * a.q;
+    const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+    const typename T::S* src = in_ptr<T>(a.send, s);
+    typename T::S* dst = out_ptr<T>(a.recv, r) + base;
+    using P = AgPolicy;
+    if ((seg + 1) * kTile <= len) {
+      const Lane<T, P, true> ln(seg, len);
+      typename Lane<T, P, true>::SV v[P::U];
+#pragma unroll
+      for (int u = 0; u < P::U; ++u) v[u] = ln.load(src, u);
+#pragma unroll
+      for (int u = 0; u < P::U; ++u) ln.store(dst, u, v[u]);
+    } else {
+      const Lane<T, P, false> ln(seg, len);
+      typename Lane<T, P, false>::SV v[P::U];
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        if (ln.on(u)) v[u] = ln.load(src, u);
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        if (ln.on(u)) ln.store(dst, u, v[u]);
+    }
+  }
+}
+
+// AllGather, software-pipelined variant (grid-stride): the next tile's
+// shard vectors are loaded before the current tile's N stores are issued.
+template <class T>
+__global__ __launch_bounds__(kBlock) void ag_pipe_kernel(ShardArgs a) {
+  using P = AgPolicy;
+  using L = Lane<T, P, false>;
+  uint64_t tile = blockIdx.x;
+  if (tile >= a.ntiles) return;
+  auto setup = [&](uint64_t t, int& s, uint64_t& seg, uint64_t& len) {
+    s = static_cast<int>(t / a.tiles_per_shard);
+    seg = t - uint64_t(s) * a.tiles_per_shard;
+    const uint64_t base = uint64_t(s) * a.q;
+    len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+  };
+  int s;
+  uint64_t seg, len;
+  setup(tile, s, seg, len);
+  L ln(seg, len);
+  typename L::SV v[P::U];
+#pragma unroll
+  for (int u = 0; u < P::U; ++u)
+    if (ln.on(u)) v[u] = ln.load(in_ptr<T>(a.send, s), u);
+  for (;;) {
+    const uint64_t next = tile + gridDim.x;
+    const bool more = next < a.ntiles;
+    int s2 = 0;
+    uint64_t seg2 = 0, len2 = 0;
+    if (more) setup(next, s2, seg2, len2);
+    L ln2(seg2, len2);
+    typename L::SV w[P::U];
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        if (ln2.on(u)) w[u] = ln2.load(in_ptr<T>(a.send, s2), u);
+    }
+    const uint64_t base = uint64_t(s) * a.q;
+    for (int r = 0; r < a.nranks; ++r) {
+      typename T::S* dst = out_ptr<T>(a.recv, r) + base;
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        if (ln.on(u)) ln.store(dst, u, v[u]);
+    }
+    if (!more) break;
+    tile = next;
+    s = s2;
+    ln = ln2;
+#pragma unroll
+    for (int u = 0; u < P::U; ++u) v[u] = w[u];
   }
 }
 
@@ -273,25 +411,26 @@ struct FlatArgs {
 // outputs ([DECOMP] §数学证明 Direct AllReduce): 2N·M elements of traffic.
 template <class T, int OP, bool FULL>
 __device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
-  using SV = typename Lane<T, FULL>::SV;
+  using P = ArPolicy;
+  using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
-  const Lane<T, FULL> ln(tile, a.count);
-  typename T::A acc[kUnroll][V];
-  fold_ranks<T, OP, FULL>(a.send, a.nranks, 0, ln, acc);
-  SV o[kUnroll];
+  const L ln(tile, a.count);
+  typename T::A acc[P::U][V];
+  fold_ranks<T, OP, P, FULL>(a.send, a.nranks, 0, ln, acc);
+  typename L::SV o[P::U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) o[u] = narrow_vec<T, FULL>(acc[u]);
+  for (int u = 0; u < P::U; ++u) o[u] = narrow_vec<T, typename L::SV>(acc[u]);
   for (int r = 0; r < a.nranks; ++r) {
     typename T::S* dst = out_ptr<T>(a.recv, r);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) ln.store(dst, u, o[u]);
   }
 }
 
 template <class T, int OP>
 __global__ __launch_bounds__(kBlock) void ar_direct_kernel(FlatArgs a) {
-  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  constexpr uint64_t kTile = tile_of<ArPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     if ((tile + 1) * kTile <= a.count)
       ar_tile<T, OP, true>(a, tile);
@@ -351,7 +490,8 @@ __device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
 template <class T, int OP, bool FULL>
 __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len) {
   using A = typename T::A;
-  using L = Lane<T, FULL>;
+  using P = RingPolicy;
+  using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const int n = a.nranks;
   const int up = mod_n(r - 1, n);
@@ -360,13 +500,13 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
   A* part = static_cast<A*>(a.partial);
   const uint64_t slot = uint64_t(n) * a.q;  // elements per generation
   const L ln(seg, len);
-  typename L::AV in[kUnroll];
-  typename L::SV own[kUnroll];
+  typename L::AV in[P::U];
+  typename L::SV own[P::U];
   const typename T::S* mine = in_ptr<T>(a.send, r) + cbase;
   if (t == 0) {
     const typename T::S* theirs = in_ptr<T>(a.send, up) + cbase;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) {
         const typename L::SV x = ln.load(theirs, u);
 #pragma unroll
@@ -375,16 +515,16 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
   } else {
     const A* theirs = part + uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) in[u] = ln.load_acc(theirs, u);
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
+  for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) own[u] = ln.load(mine, u);
   if (!last) {
     A* dst = part + uint64_t(t & 1) * slot + uint64_t(r) * a.q;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < P::U; ++u) {
       if (!ln.on(u)) continue;
       typename L::AV v;
 #pragma unroll
@@ -394,7 +534,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
   } else {
     typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, r) + cbase : out_ptr<T>(a.recv, c);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < P::U; ++u) {
       if (!ln.on(u)) continue;
       typename L::SV v;
 #pragma unroll
@@ -408,20 +548,21 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
 // the stand-alone AllGather's own-shard placement).
 template <class T, bool FULL>
 __device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, uint64_t seg, uint64_t len) {
-  using L = Lane<T, FULL>;
+  using P = RingPolicy;
+  using L = Lane<T, P, FULL>;
   const L ln(seg, len);
-  typename L::SV v[kUnroll];
+  typename L::SV v[P::U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
+  for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) v[u] = ln.load(src, u);
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
+  for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) ln.store(dst, u, v[u]);
 }
 
 template <class T, int OP>
 __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
-  constexpr uint64_t kTile = tile_of(vec_elems<T>());
+  constexpr uint64_t kTile = tile_of<RingPolicy>(vec_elems<T>());
   const int n = a.nranks;
   const int r = static_cast<int>(tile / a.tiles_per_chunk);
   const uint64_t seg = tile - uint64_t(r) * a.tiles_per_chunk;
@@ -534,23 +675,47 @@ struct PadArgs {
 template <class T, int OP>
 __global__ __launch_bounds__(kBlock) void pad_kernel(PadArgs a) {
   using S = typename T::S;
+  using P = PadPolicy;
   constexpr int V = vec_elems<T>();
-  constexpr uint64_t kTile = uint64_t(kBlock) * V;
+  constexpr uint64_t kTile = tile_of<P>(V);
   const S ident = T::narrow(identity<T, OP>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int r = static_cast<int>(tile / a.tiles_per_rank);
     const uint64_t seg = tile - uint64_t(r) * a.tiles_per_rank;
     const S* src = in_ptr<T>(a.src, r);
     S* dst = out_ptr<T>(a.dst, r);
-    const uint64_t j = seg * kTile + uint64_t(threadIdx.x) * V;
+    const uint64_t lo = seg * kTile, hi = lo + kTile;
+    if (hi <= a.count) {
+      // wholly inside the copied range: a plain vector copy (nothing to do in place)
+      if (src != dst) {
+        const Lane<T, P, true> ln(seg, a.count);
+        typename Lane<T, P, true>::SV v[P::U];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const uint64_t i = j + k;
-      if (i < a.count) {
-        if (src != dst) dst[i] = src[i];
-      } else if (i < a.padded) {
-        dst[i] = ident;
+        for (int u = 0; u < P::U; ++u) v[u] = ln.load(src, u);
+#pragma unroll
+        for (int u = 0; u < P::U; ++u) ln.store(dst, u, v[u]);
       }
+    } else if (lo >= a.count && hi <= a.padded) {
+      // wholly inside the pad: vector stores of the identity
+      const Lane<T, P, true> ln(seg, a.padded);
+      typename Lane<T, P, true>::SV v;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = ident;
+#pragma unroll
+      for (int u = 0; u < P::U; ++u) ln.store(dst, u, v);
+    } else {
+      // the tile holding the boundary (or the end): element by element
+      const Lane<T, P, false> ln(seg, a.padded);
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        for (int k = 0; k < ln.cnt[u]; ++k) {
+          const uint64_t i = ln.j[u] + k;
+          if (i < a.count) {
+            if (src != dst) put1(dst + i, get1(src + i));
+          } else {
+            put1(dst + i, ident);
+          }
+        }
     }
   }
 }
@@ -590,8 +755,11 @@ hipError_t by_op(int op, F&& f) {
   }
 }
 
+// Grid cap in workgroups per CU.  The default is high enough that every
+// workload here gets one workgroup per tile (measured faster than a capped
+// grid-stride loop for all kernels); the loop only matters past it.
 #ifndef CCL_SIM_BLOCKS_PER_CU
-#define CCL_SIM_BLOCKS_PER_CU 64
+#define CCL_SIM_BLOCKS_PER_CU 1024
 #endif
 
 unsigned grid_for(uint64_t ntiles, int num_cus) {
@@ -600,9 +768,9 @@ unsigned grid_for(uint64_t ntiles, int num_cus) {
   return static_cast<unsigned>(g > 0 ? g : 1);
 }
 
-template <class T>
+template <class T, class P>
 uint64_t tile_elems() {
-  return uint64_t(kBlock) * vec_elems<T>() * kUnroll;
+  return tile_of<P>(vec_elems<T>());
 }
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
@@ -639,14 +807,13 @@ size_t accum_size(int dtype) { return dtype == kBFloat16 ? 4 : elem_size(dtype);
 
 hipError_t run_direct(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    const uint64_t tile = tile_elems<T>();
     if (c.coll == kAllReduce) {
       FlatArgs a{};
       a.send = c.send;
       a.recv = c.recv;
       a.nranks = c.nranks;
       a.count = c.limit;
-      a.ntiles = ceil_div(c.limit, tile);
+      a.ntiles = ceil_div(c.limit, tile_elems<T, ArPolicy>());
       const unsigned grid = grid_for(a.ntiles, c.num_cus);
       return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
         hipLaunchKernelGGL((ar_direct_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
@@ -658,7 +825,8 @@ hipError_t run_direct(const Call& c) {
     a.recv = c.recv;
     a.nranks = c.nranks;
     a.q = c.q;
-    a.tiles_per_shard = ceil_div(c.q, tile);
+    a.tiles_per_shard =
+        ceil_div(c.q, c.coll == kReduceScatter ? tile_elems<T, RsPolicy>() : tile_elems<T, AgPolicy>());
     a.ntiles = uint64_t(c.nranks) * a.tiles_per_shard;
     a.limit = c.limit;
     const unsigned grid = grid_for(a.ntiles, c.num_cus);
@@ -668,6 +836,26 @@ hipError_t run_direct(const Call& c) {
         return hipGetLastError();
       });
     }
+#ifndef CCL_SIM_AG_MODE
+#define CCL_SIM_AG_MODE 0
+#endif
+#ifndef CCL_SIM_AG_PIPE_PER_CU
+#define CCL_SIM_AG_PIPE_PER_CU 8
+#endif
+    if (CCL_SIM_AG_MODE == 2) {
+      const uint64_t g = uint64_t(c.num_cus) * CCL_SIM_AG_PIPE_PER_CU;
+      const unsigned gp = static_cast<unsigned>(g < a.ntiles ? g : a.ntiles);
+      hipLaunchKernelGGL((ag_pipe_kernel<T>), dim3(gp), dim3(kBlock), 0, c.stream, a);
+      return hipGetLastError();
+    }
+    if (CCL_SIM_AG_MODE == 1) {
+      const uint64_t groups = ceil_div(a.ntiles, 8);
+      const uint64_t nitems = groups * 8 * uint64_t(c.nranks);
+      uint64_t g = grid_for(nitems, c.num_cus);
+      g = (g + 7) / 8 * 8;
+      hipLaunchKernelGGL((ag_xcd_kernel<T>), dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, c.stream, a, nitems);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid), dim3(kBlock), 0, c.stream, a);
     return hipGetLastError();
   });
@@ -675,7 +863,7 @@ hipError_t run_direct(const Call& c) {
 
 hipError_t run_ring_stepwise(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    RingArgs a = make_ring_args(c, tile_elems<T>());
+    RingArgs a = make_ring_args(c, tile_elems<T, RingPolicy>());
     const unsigned grid = grid_for(a.ntiles, c.num_cus);
     const int n = c.nranks;
     const int nsteps = (c.coll == kAllReduce) ? 2 * (n - 1) : (c.coll == kReduceScatter ? n - 1 : n);
@@ -693,11 +881,16 @@ hipError_t run_ring_stepwise(const Call& c) {
   });
 }
 
-hipError_t run_ring_persistent(const Call& c, bool* unsupported) {
+#ifndef CCL_SIM_PERSISTENT_PER_CU
+#define CCL_SIM_PERSISTENT_PER_CU 2
+#endif
+
+hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
   *unsupported = false;
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    RingArgs a = make_ring_args(c, tile_elems<T>());
+    RingArgs a = make_ring_args(c, tile_elems<T, RingPolicy>());
     a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+    if (c.spin_limit) a.spin_limit = c.spin_limit;
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
       auto kernel = ring_persistent_kernel<U, OP>;
@@ -708,9 +901,21 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported) {
         *unsupported = true;
         return hipSuccess;
       }
-      uint64_t grid = uint64_t(per_cu) * uint64_t(c.num_cus);
+      // Workgroups per CU: at most what the occupancy calculation allows,
+      // and by default only CCL_SIM_PERSISTENT_PER_CU of them: a grid at
+      // the full occupancy figure was found not to be co-resident (its
+      // first barrier ran into the poll limit).
+      const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
+      const int use = want < per_cu ? want : per_cu;
+      uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
       if (grid > a.ntiles) grid = a.ntiles;
       if (grid == 0) grid = 1;
+      if (plan) {
+        plan->occupancy_per_cu = per_cu;
+        plan->per_cu = use;
+        plan->grid = grid;
+        plan->tiles_per_step = a.ntiles;
+      }
       hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -729,7 +934,7 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported) {
 
 hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    const uint64_t tile = uint64_t(kBlock) * vec_elems<T>();
+    const uint64_t tile = tile_elems<T, PadPolicy>();
     PadArgs a{};
     a.src = c.send;
     a.dst = c.recv;
