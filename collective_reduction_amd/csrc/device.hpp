@@ -11,10 +11,6 @@
 
 namespace ccl {
 
-#ifndef CCL_SIM_BLOCK
-#define CCL_SIM_BLOCK 256
-#endif
-constexpr int kBlock = CCL_SIM_BLOCK;  // threads per workgroup (256 = 4 wave64s)
 constexpr int kInlineRanks = 64;  // rank pointers passed in the kernel arguments
 
 #ifndef CCL_SIM_RANK_BATCH

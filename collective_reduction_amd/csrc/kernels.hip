@@ -9,8 +9,9 @@
 //   [WHY-EQ] "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
 //
 // Work decomposition.  Every kernel is a grid-stride loop over tiles of
-// kBlock·V·U elements (V = 16 / sizeof(element): one 128-bit access per
-// lane per vector, U vectors per lane; U is part of each kernel's Policy).  A tile never crosses a shard (or ring chunk)
+// TB·V·U elements (V = 16 / sizeof(element): one 128-bit access per lane
+// per vector, U vectors per lane, TB lanes; TB and U are part of each
+// kernel's Policy).  A tile never crosses a shard (or ring chunk)
 // boundary, so the shard a tile belongs to is one scalar division per tile
 // and the shard-local side of every access keeps the buffer's alignment;
 // the other side (the input of ReduceScatter at r·q + j, the output of
@@ -37,39 +38,48 @@ constexpr int vec_elems() {
   return 16 / static_cast<int>(sizeof(typename T::S));
 }
 
-// Per-kernel memory policy: U 128-bit vectors per lane per tile, and
-// whether rank-buffer loads / stores carry the nontemporal hint.  Every
+// Per-kernel shape and memory policy: TB threads per workgroup, U 128-bit
+// vectors per lane per tile, and whether rank-buffer loads / stores carry
+// the nontemporal hint.  Every
 // rank buffer is streamed once per call, so keeping it out of the caches
 // pays where a kernel mostly reads (ReduceScatter, AllReduce, ring steps);
 // the AllGather, which writes N times what it reads, is faster with
 // ordinary accesses.  Each default can be replaced at build time.
-template <int U_, bool NTL_, bool NTS_>
+template <int TB_, int U_, bool NTL_, bool NTS_>
 struct Policy {
+  static constexpr int TB = TB_;  // threads per workgroup
   static constexpr int U = U_;
   static constexpr bool NTL = NTL_;
   static constexpr bool NTS = NTS_;
 };
 #ifndef CCL_SIM_RS_POLICY
-#define CCL_SIM_RS_POLICY 4, true, true
+#define CCL_SIM_RS_POLICY 256, 1, true, true
 #endif
 #ifndef CCL_SIM_AG_POLICY
-#define CCL_SIM_AG_POLICY 4, false, false
+#define CCL_SIM_AG_POLICY 256, 1, true, false
 #endif
 #ifndef CCL_SIM_AR_POLICY
-#define CCL_SIM_AR_POLICY 4, true, true
+#define CCL_SIM_AR_POLICY 256, 1, true, true
 #endif
 #ifndef CCL_SIM_RING_POLICY
-#define CCL_SIM_RING_POLICY 4, true, true
+#define CCL_SIM_RING_POLICY 256, 1, true, true
+#endif
+#ifndef CCL_SIM_PERSIST_POLICY
+#define CCL_SIM_PERSIST_POLICY 256, 4, true, true
+#endif
+#ifndef CCL_SIM_PAD_POLICY
+#define CCL_SIM_PAD_POLICY 256, 4, false, false
 #endif
 using RsPolicy = Policy<CCL_SIM_RS_POLICY>;
 using AgPolicy = Policy<CCL_SIM_AG_POLICY>;
 using ArPolicy = Policy<CCL_SIM_AR_POLICY>;
 using RingPolicy = Policy<CCL_SIM_RING_POLICY>;
-using PadPolicy = Policy<4, false, false>;
+using PersistPolicy = Policy<CCL_SIM_PERSIST_POLICY>;
+using PadPolicy = Policy<CCL_SIM_PAD_POLICY>;
 
 template <class P>
 constexpr uint64_t tile_of(int v) {
-  return uint64_t(kBlock) * uint64_t(v) * P::U;
+  return uint64_t(P::TB) * uint64_t(v) * P::U;
 }
 
 // K elements of E as one vector value, promising only element alignment.
@@ -109,6 +119,8 @@ __device__ inline void put1(E* p, E v) {
   *(CCL_GLOBAL E*)(p) = v;
 }
 
+__device__ inline int rank_of_tile(uint64_t tile, uint64_t per) { return static_cast<int>(tile / per); }
+
 __device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
   return j < len ? static_cast<int>(len - j < static_cast<uint64_t>(v) ? len - j : static_cast<uint64_t>(v)) : 0;
 }
@@ -131,7 +143,7 @@ struct Lane {
   __device__ Lane(uint64_t seg, uint64_t len) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      j[u] = seg * tile_of<P>(V) + uint64_t(u * kBlock + static_cast<int>(threadIdx.x)) * V;
+      j[u] = seg * tile_of<P>(V) + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * V;
       cnt[u] = FULL ? V : lane_count(j[u], len, V);
     }
   }
@@ -248,10 +260,10 @@ __device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
 }
 
 template <class T, int OP>
-__global__ __launch_bounds__(kBlock) void rs_direct_kernel(ShardArgs a) {
+__global__ __launch_bounds__(RsPolicy::TB) void rs_direct_kernel(ShardArgs a) {
   constexpr uint64_t kTile = tile_of<RsPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-    const int r = static_cast<int>(tile / a.tiles_per_shard);
+    const int r = rank_of_tile(tile, a.tiles_per_shard);
     const uint64_t seg = tile - uint64_t(r) * a.tiles_per_shard;
     if ((seg + 1) * kTile <= a.q)
       rs_tile<T, OP, true>(a, r, seg);
@@ -263,12 +275,8 @@ __global__ __launch_bounds__(kBlock) void rs_direct_kernel(ShardArgs a) {
 // AllGather: recv[r][s·q + j] = send[s][j] for every r, positions below
 // `limit` only ([DECOMP] §数学证明 AllGather, trim of §Contract 实验四).
 // Each shard vector is read once into registers and stored N times.
-#ifndef CCL_SIM_AG_ROTATE
-#define CCL_SIM_AG_ROTATE 0
-#endif
-
 template <class T, bool FULL>
-__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len, uint64_t tile) {
+__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
   using P = AgPolicy;
   using L = Lane<T, P, FULL>;
   const L ln(seg, len);
@@ -278,12 +286,7 @@ __device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t
 #pragma unroll
   for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) v[u] = ln.load(src, u);
-  // With CCL_SIM_AG_ROTATE each tile starts its N stores at a different
-  // rank, spreading concurrent writes over all output buffers.
-  const int first = CCL_SIM_AG_ROTATE ? static_cast<int>(tile % uint64_t(a.nranks)) : 0;
-  for (int i = 0; i < a.nranks; ++i) {
-    int r = first + i;
-    if (r >= a.nranks) r -= a.nranks;
+  for (int r = 0; r < a.nranks; ++r) {
     typename T::S* dst = out_ptr<T>(a.recv, r) + base;
 #pragma unroll
     for (int u = 0; u < P::U; ++u)
@@ -292,111 +295,17 @@ __device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t
 }
 
 template <class T>
-__global__ __launch_bounds__(kBlock) void ag_direct_kernel(ShardArgs a) {
+__global__ __launch_bounds__(AgPolicy::TB) void ag_direct_kernel(ShardArgs a) {
   constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-    const int s = static_cast<int>(tile / a.tiles_per_shard);
+    const int s = rank_of_tile(tile, a.tiles_per_shard);
     const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
     const uint64_t base = uint64_t(s) * a.q;
     const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
     if ((seg + 1) * kTile <= len)
-      ag_tile<T, true>(a, s, seg, len, tile);
+      ag_tile<T, true>(a, s, seg, len);
     else
-      ag_tile<T, false>(a, s, seg, len, tile);
-  }
-}
-
-// AllGather, XCD-aware variant: one work item copies one shard tile to ONE
-// output rank.  Item i runs on XCD i mod 8 (workgroups are dealt to the
-// eight XCDs round-robin and the grid is a multiple of 8), and the N items
-// of a shard tile are numbered 8 apart, so they land on the same XCD at
-// about the same time: the shard tile comes from HBM once and from that
-// XCD's L2 for the other N-1 copies, while every workgroup streams a single
-// output buffer.
-template <class T>
-__global__ __launch_bounds__(kBlock) void ag_xcd_kernel(ShardArgs a, uint64_t nitems) {
-  constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
-  const uint64_t n = uint64_t(a.nranks);
-  for (uint64_t i = blockIdx.x; i < nitems; i += gridDim.x) {
-    const uint64_t l = i / 8;
-    const uint64_t st = (l / n) * 8 + (i % 8);  // shard tile
-    const int r = static_cast<int>(l % n);      // output rank
-    if (st >= a.ntiles) continue;
-    const int s = static_cast<int>(st / a.tiles_per_shard);
-    const uint64_t seg = st - uint64_t(s) * a.tiles_per_shard;
-    const uint64_t base = uint64_t(s) * a.q;
-    const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
-    const typename T::S* src = in_ptr<T>(a.send, s);
-    typename T::S* dst = out_ptr<T>(a.recv, r) + base;
-    using P = AgPolicy;
-    if ((seg + 1) * kTile <= len) {
-      const Lane<T, P, true> ln(seg, len);
-      typename Lane<T, P, true>::SV v[P::U];
-#pragma unroll
-      for (int u = 0; u < P::U; ++u) v[u] = ln.load(src, u);
-#pragma unroll
-      for (int u = 0; u < P::U; ++u) ln.store(dst, u, v[u]);
-    } else {
-      const Lane<T, P, false> ln(seg, len);
-      typename Lane<T, P, false>::SV v[P::U];
-#pragma unroll
-      for (int u = 0; u < P::U; ++u)
-        if (ln.on(u)) v[u] = ln.load(src, u);
-#pragma unroll
-      for (int u = 0; u < P::U; ++u)
-        if (ln.on(u)) ln.store(dst, u, v[u]);
-    }
-  }
-}
-
-// AllGather, software-pipelined variant (grid-stride): the next tile's
-// shard vectors are loaded before the current tile's N stores are issued.
-template <class T>
-__global__ __launch_bounds__(kBlock) void ag_pipe_kernel(ShardArgs a) {
-  using P = AgPolicy;
-  using L = Lane<T, P, false>;
-  uint64_t tile = blockIdx.x;
-  if (tile >= a.ntiles) return;
-  auto setup = [&](uint64_t t, int& s, uint64_t& seg, uint64_t& len) {
-    s = static_cast<int>(t / a.tiles_per_shard);
-    seg = t - uint64_t(s) * a.tiles_per_shard;
-    const uint64_t base = uint64_t(s) * a.q;
-    len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
-  };
-  int s;
-  uint64_t seg, len;
-  setup(tile, s, seg, len);
-  L ln(seg, len);
-  typename L::SV v[P::U];
-#pragma unroll
-  for (int u = 0; u < P::U; ++u)
-    if (ln.on(u)) v[u] = ln.load(in_ptr<T>(a.send, s), u);
-  for (;;) {
-    const uint64_t next = tile + gridDim.x;
-    const bool more = next < a.ntiles;
-    int s2 = 0;
-    uint64_t seg2 = 0, len2 = 0;
-    if (more) setup(next, s2, seg2, len2);
-    L ln2(seg2, len2);
-    typename L::SV w[P::U];
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < P::U; ++u)
-        if (ln2.on(u)) w[u] = ln2.load(in_ptr<T>(a.send, s2), u);
-    }
-    const uint64_t base = uint64_t(s) * a.q;
-    for (int r = 0; r < a.nranks; ++r) {
-      typename T::S* dst = out_ptr<T>(a.recv, r) + base;
-#pragma unroll
-      for (int u = 0; u < P::U; ++u)
-        if (ln.on(u)) ln.store(dst, u, v[u]);
-    }
-    if (!more) break;
-    tile = next;
-    s = s2;
-    ln = ln2;
-#pragma unroll
-    for (int u = 0; u < P::U; ++u) v[u] = w[u];
+      ag_tile<T, false>(a, s, seg, len);
   }
 }
 
@@ -429,7 +338,7 @@ __device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
 }
 
 template <class T, int OP>
-__global__ __launch_bounds__(kBlock) void ar_direct_kernel(FlatArgs a) {
+__global__ __launch_bounds__(ArPolicy::TB) void ar_direct_kernel(FlatArgs a) {
   constexpr uint64_t kTile = tile_of<ArPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     if ((tile + 1) * kTile <= a.count)
@@ -487,10 +396,9 @@ __device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
 // out_r[chunk c] (the AllGather phase's source: the phase boundary fused
 // in one state machine as in [DECOMP] §源码三), ReduceScatter into
 // recvbufs[c], c = r+1.
-template <class T, int OP, bool FULL>
+template <class T, int OP, class P, bool FULL>
 __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len) {
   using A = typename T::A;
-  using P = RingPolicy;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const int n = a.nranks;
@@ -546,9 +454,8 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
 
 // Copy of `len` elements from src to dst for one tile (AllGather steps and
 // the stand-alone AllGather's own-shard placement).
-template <class T, bool FULL>
+template <class T, class P, bool FULL>
 __device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, uint64_t seg, uint64_t len) {
-  using P = RingPolicy;
   using L = Lane<T, P, FULL>;
   const L ln(seg, len);
   typename L::SV v[P::U];
@@ -560,11 +467,11 @@ __device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, u
     if (ln.on(u)) ln.store(dst, u, v[u]);
 }
 
-template <class T, int OP>
+template <class T, int OP, class P>
 __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
-  constexpr uint64_t kTile = tile_of<RingPolicy>(vec_elems<T>());
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   const int n = a.nranks;
-  const int r = static_cast<int>(tile / a.tiles_per_chunk);
+  const int r = rank_of_tile(tile, a.tiles_per_chunk);
   const uint64_t seg = tile - uint64_t(r) * a.tiles_per_chunk;
   int c;
   bool reduce = false;
@@ -593,21 +500,21 @@ __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
   const bool full = (seg + 1) * kTile <= len;
   if (reduce) {
     if (full)
-      ring_rs_tile<T, OP, true>(a, step, r, seg, c, len);
+      ring_rs_tile<T, OP, P, true>(a, step, r, seg, c, len);
     else
-      ring_rs_tile<T, OP, false>(a, step, r, seg, c, len);
+      ring_rs_tile<T, OP, P, false>(a, step, r, seg, c, len);
   } else {
     typename T::S* dst = out_ptr<T>(a.recv, r) + uint64_t(c) * a.q;
     if (full)
-      copy_tile<T, true>(src, dst, seg, len);
+      copy_tile<T, P, true>(src, dst, seg, len);
     else
-      copy_tile<T, false>(src, dst, seg, len);
+      copy_tile<T, P, false>(src, dst, seg, len);
   }
 }
 
 template <class T, int OP>
-__global__ __launch_bounds__(kBlock) void ring_step_kernel(RingArgs a) {
-  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP>(a, a.step, tile);
+__global__ __launch_bounds__(RingPolicy::TB) void ring_step_kernel(RingArgs a) {
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, RingPolicy>(a, a.step, tile);
 }
 
 // Grid-wide barrier for the persistent ring.  Every workgroup of the grid
@@ -645,7 +552,7 @@ __device__ inline bool grid_barrier(unsigned* ctrl, unsigned target, unsigned sp
 }
 
 template <class T, int OP>
-__global__ __launch_bounds__(kBlock) void ring_persistent_kernel(RingArgs a) {
+__global__ __launch_bounds__(PersistPolicy::TB) void ring_persistent_kernel(RingArgs a) {
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
   unsigned arrivals = 0;
@@ -654,7 +561,7 @@ __global__ __launch_bounds__(kBlock) void ring_persistent_kernel(RingArgs a) {
       arrivals += gridDim.x;
       if (!grid_barrier(a.ctrl, arrivals, a.spin_limit)) return;
     }
-    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP>(a, step, tile);
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, PersistPolicy>(a, step, tile);
   }
 }
 
@@ -673,14 +580,14 @@ struct PadArgs {
 };
 
 template <class T, int OP>
-__global__ __launch_bounds__(kBlock) void pad_kernel(PadArgs a) {
+__global__ __launch_bounds__(PadPolicy::TB) void pad_kernel(PadArgs a) {
   using S = typename T::S;
   using P = PadPolicy;
   constexpr int V = vec_elems<T>();
   constexpr uint64_t kTile = tile_of<P>(V);
   const S ident = T::narrow(identity<T, OP>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-    const int r = static_cast<int>(tile / a.tiles_per_rank);
+    const int r = rank_of_tile(tile, a.tiles_per_rank);
     const uint64_t seg = tile - uint64_t(r) * a.tiles_per_rank;
     const S* src = in_ptr<T>(a.src, r);
     S* dst = out_ptr<T>(a.dst, r);
@@ -816,7 +723,7 @@ hipError_t run_direct(const Call& c) {
       a.ntiles = ceil_div(c.limit, tile_elems<T, ArPolicy>());
       const unsigned grid = grid_for(a.ntiles, c.num_cus);
       return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
-        hipLaunchKernelGGL((ar_direct_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        hipLaunchKernelGGL((ar_direct_kernel<U, OP>), dim3(grid), dim3(ArPolicy::TB), 0, c.stream, a);
         return hipGetLastError();
       });
     }
@@ -832,31 +739,11 @@ hipError_t run_direct(const Call& c) {
     const unsigned grid = grid_for(a.ntiles, c.num_cus);
     if (c.coll == kReduceScatter) {
       return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
-        hipLaunchKernelGGL((rs_direct_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        hipLaunchKernelGGL((rs_direct_kernel<U, OP>), dim3(grid), dim3(RsPolicy::TB), 0, c.stream, a);
         return hipGetLastError();
       });
     }
-#ifndef CCL_SIM_AG_MODE
-#define CCL_SIM_AG_MODE 0
-#endif
-#ifndef CCL_SIM_AG_PIPE_PER_CU
-#define CCL_SIM_AG_PIPE_PER_CU 8
-#endif
-    if (CCL_SIM_AG_MODE == 2) {
-      const uint64_t g = uint64_t(c.num_cus) * CCL_SIM_AG_PIPE_PER_CU;
-      const unsigned gp = static_cast<unsigned>(g < a.ntiles ? g : a.ntiles);
-      hipLaunchKernelGGL((ag_pipe_kernel<T>), dim3(gp), dim3(kBlock), 0, c.stream, a);
-      return hipGetLastError();
-    }
-    if (CCL_SIM_AG_MODE == 1) {
-      const uint64_t groups = ceil_div(a.ntiles, 8);
-      const uint64_t nitems = groups * 8 * uint64_t(c.nranks);
-      uint64_t g = grid_for(nitems, c.num_cus);
-      g = (g + 7) / 8 * 8;
-      hipLaunchKernelGGL((ag_xcd_kernel<T>), dim3(static_cast<unsigned>(g)), dim3(kBlock), 0, c.stream, a, nitems);
-      return hipGetLastError();
-    }
-    hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+    hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid), dim3(AgPolicy::TB), 0, c.stream, a);
     return hipGetLastError();
   });
 }
@@ -872,7 +759,7 @@ hipError_t run_ring_stepwise(const Call& c) {
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
       for (int step = first; step < nsteps; ++step) {
         a.step = step;
-        hipLaunchKernelGGL((ring_step_kernel<U, OP>), dim3(grid), dim3(kBlock), 0, c.stream, a);
+        hipLaunchKernelGGL((ring_step_kernel<U, OP>), dim3(grid), dim3(RingPolicy::TB), 0, c.stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
@@ -888,14 +775,14 @@ hipError_t run_ring_stepwise(const Call& c) {
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
   *unsupported = false;
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    RingArgs a = make_ring_args(c, tile_elems<T, RingPolicy>());
+    RingArgs a = make_ring_args(c, tile_elems<T, PersistPolicy>());
     a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
     if (c.spin_limit) a.spin_limit = c.spin_limit;
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
       auto kernel = ring_persistent_kernel<U, OP>;
       int per_cu = 0;
-      hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
+      hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, PersistPolicy::TB, 0);
       if (e != hipSuccess) return e;
       if (per_cu <= 0 || c.num_cus <= 0) {
         *unsupported = true;
@@ -921,7 +808,7 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan*
       if (e != hipSuccess) return e;
       void* args[] = {&a};
       e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)),
-                                     dim3(kBlock), args, 0, c.stream);
+                                     dim3(PersistPolicy::TB), args, 0, c.stream);
       if (e == hipErrorCooperativeLaunchTooLarge) {
         (void)hipGetLastError();
         *unsupported = true;
@@ -945,7 +832,7 @@ hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded) {
     a.ntiles = uint64_t(c.nranks) * a.tiles_per_rank;
     const unsigned grid = grid_for(a.ntiles, c.num_cus);
     auto go = [&](auto kernel) -> hipError_t {
-      hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, c.stream, a);
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(PadPolicy::TB), 0, c.stream, a);
       return hipGetLastError();
     };
     switch (c.op) {
