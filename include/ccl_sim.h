@@ -3,8 +3,9 @@
  * whose buffers all live in one AMD MI355X (gfx950) GPU's HBM.
  *
  * One call covers all N ranks, the way a single host process drives every
- * rank with grouped calls in the Nsight probe of "NCCL 专家课程 07：AllReduce
- * 等价分解、显存生命周期与 Kernel 证据" (blog.cptz.space), §Kernel 证据.  The
+ * rank with grouped calls in the native probe of "NCCL 专家课程 07：AllReduce
+ * 等价分解、显存生命周期与 Kernel 证据" (blog.cptz.space), §Nsight 实验如何避免
+ * 框架噪声.  The
  * "links" between ranks are HBM reads and writes; there is no second GPU.
  *
  * Pages cited below:
@@ -32,8 +33,9 @@
  *            take the fastest path; any other layout is handled, slower.
  * Streams.   Work is enqueued on `stream` (a hipStream_t; NULL is the null
  *            stream) and the call returns without waiting.  Buffers must stay
- *            alive until that stream work completes ([DECOMP] §显存生命周期:
- *            a buffer's lifetime ends with the last kernel that reads it).
+ *            alive until that stream work completes ([DECOMP] §显存实验必须区分
+ *            steady 与 peak: freeing a buffer before the collective has read
+ *            it is unsafe).
  * Workspace. Device scratch of at least ccl_sim_workspace_size(...) bytes,
  *            256-byte aligned, owned by the caller.  It carries the device
  *            copy of the pointer tables when nranks > 64, the partial sums
