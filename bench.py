@@ -224,6 +224,9 @@ def main():
     secondary = {}
     if not args.no_secondary:
         secondary = run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, args.secondary_iters)
+        del send, shards, recv
+        torch.cuda.empty_cache()
+        secondary.update(run_many_ranks(cs, torch, stream, args.secondary_iters))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -314,8 +317,65 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
             send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
     timed("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
           ab("reduce_scatter", n, m, dtype, "direct"))
+    # smaller M on prefixes of the same buffers (N=8, M = 2^24 and 2^26)
+    for lg in (24, 26):
+        mm = 1 << lg
+        if mm >= m or mm % n:
+            continue
+        qq = mm // n
+        sv = [t[:mm] for t in send]
+        rv = [t[:mm] for t in recv]
+        hv = [t[:qq] for t in shards]
+        for sched in ("direct", "ring_stepwise"):
+            timed(f"rs_ag_{sched}_m2^{lg}", lambda s=sched, sv=sv, rv=rv, hv=hv, mm=mm, qq=qq: (
+                cs.ccl_sim_reduce_scatter(sv, hv, mm, qq, schedule=s, workspace=ws, stream=stream),
+                cs.ccl_sim_all_gather(hv, rv, qq, mm, schedule=s, workspace=ws, stream=stream)),
+                ab("reduce_scatter", n, mm, dtype, sched) + ab("all_gather", n, mm, dtype, sched))
     # plain copy of the same size as one rank's buffer, for scale
     timed("copy_one_rank_torch", lambda: recv[0].copy_(send[0]), 2 * m * send[0].element_size())
+    return res
+
+
+def run_many_ranks(cs, torch, stream, iters):
+    """The 256-rank workloads (M=2^22 float32; the 6,553,600-element bf16
+    bucket) on freshly drawn device buffers: every schedule's AllReduce and
+    the direct RS+AG, timed with HIP events."""
+    res = {}
+    ab = cs.ccl_sim_algorithmic_bytes
+    for name, m, tdt, dtype in (("256x4194304_fp32", 1 << 22, torch.float32, "float32"),
+                                ("256x6553600_bf16", 6_553_600, torch.bfloat16, "bfloat16")):
+        n = 256
+        q = m // n
+        send = [torch.randn(m, device="cuda").mul_(1e-3).to(tdt) for _ in range(n)]
+        recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
+        shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
+        ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
+                                   for s in ("direct", "ring_stepwise", "ring_persistent")])
+        torch.cuda.synchronize()
+
+        def timed(key, fn, nbytes):
+            fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            st = stats([a.elapsed_time(b) for a, b in ev])
+            res[f"{key}_{name}"] = {"bytes": nbytes, "gbs": nbytes / (st["median_ms"] / 1e3) / 1e9,
+                                    "frac_of_peak": nbytes / (st["median_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, **st}
+            log(f"{key}_{name}: {st['median_ms']:.3f} ms, {res[f'{key}_{name}']['gbs']:.0f} GB/s")
+
+        for sched in ("direct", "ring_stepwise", "ring_persistent"):
+            timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(send, recv, m, schedule=s, workspace=ws,
+                                                                            stream=stream),
+                  ab("allreduce", n, m, dtype, sched))
+        timed("rs_ag_direct", lambda: (cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
+                                       cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),
+              ab("reduce_scatter", n, m, dtype, "direct") + ab("all_gather", n, m, dtype, "direct"))
+        del send, recv, shards, ws
+        torch.cuda.empty_cache()
     return res
 
 

@@ -520,18 +520,21 @@ __global__ __launch_bounds__(RingPolicy::TB) void ring_step_kernel(RingArgs a) {
 // Grid-wide barrier for the persistent ring.  Every workgroup of the grid
 // is co-resident (cooperative launch), arrives once per step on a counter
 // that only grows, and waits until all gridDim.x arrivals of this step are
-// in.  Every wave fences at device scope before the arrival (its stores are
-// complete and written back out of its XCD's L2) and again after the wait
-// (stale lines are dropped), so a workgroup's HBM stores of one step are
-// seen by every other workgroup's loads of the next, across all eight XCDs
-// and their separate L2 caches.  The wait is bounded: after spin_limit polls
-// it raises the abort word, and every workgroup that sees the word stops,
-// so the grid always drains.
+// in.  Before arriving, every wave waits until its own stores have reached
+// its XCD's L2 (vmcnt 0); one lane per workgroup then fences at device
+// scope, which writes that L2's dirty lines back to memory, arrives, polls,
+// and fences again after the wait, which drops stale L1 / L2 lines.  A
+// workgroup's HBM stores of one step are therefore seen by every other
+// workgroup's loads of the next, across all eight XCDs and their separate
+// L2 caches.  The wait is bounded: after spin_limit polls it raises the
+// abort word, and every workgroup that sees the word stops, so the grid
+// always drains.
 __device__ inline bool grid_barrier(unsigned* ctrl, unsigned target, unsigned spin_limit) {
   __shared__ int s_ok;
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
+    __threadfence();
     __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int ok = 1;
     unsigned spins = 0;
@@ -542,12 +545,12 @@ __device__ inline bool grid_barrier(unsigned* ctrl, unsigned target, unsigned sp
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(2);
     }
+    __threadfence();
     s_ok = ok;
   }
   __syncthreads();
-  __threadfence();
   return s_ok != 0;
 }
 
@@ -769,7 +772,7 @@ hipError_t run_ring_stepwise(const Call& c) {
 }
 
 #ifndef CCL_SIM_PERSISTENT_PER_CU
-#define CCL_SIM_PERSISTENT_PER_CU 2
+#define CCL_SIM_PERSISTENT_PER_CU 1
 #endif
 
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
@@ -789,9 +792,11 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan*
         return hipSuccess;
       }
       // Workgroups per CU: at most what the occupancy calculation allows,
-      // and by default only CCL_SIM_PERSISTENT_PER_CU of them: a grid at
-      // the full occupancy figure was found not to be co-resident (its
-      // first barrier ran into the poll limit).
+      // and by default only CCL_SIM_PERSISTENT_PER_CU of them.  A grid at
+      // the full occupancy figure was found not to be co-resident on MI355X
+      // (its first barrier ran into the poll limit); of the grids that are,
+      // one workgroup per CU measured fastest, since every barrier costs
+      // each workgroup an L2 write-back.
       const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
       const int use = want < per_cu ? want : per_cu;
       uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
