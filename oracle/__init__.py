@@ -31,12 +31,14 @@ Modules
 ``ring``        the ring schedule stepped literally rank by rank, with its
                 routing table and per-step state.
 ``scalar``      a pure-Python scalar twin of the above for tiny inputs.
+``recursive``   recursive-halving ReduceScatter and recursive-doubling
+                AllGather (N a power of two), stepped rank by rank.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values the
 pages print, closed forms, brute force and invariants; nothing here is
 "parity unpinned".
 """
 
-from . import reduction, collectives, ring, scalar  # noqa: F401
+from . import reduction, collectives, ring, scalar, recursive  # noqa: F401
 
-__all__ = ["reduction", "collectives", "ring", "scalar"]
+__all__ = ["reduction", "collectives", "ring", "scalar", "recursive"]

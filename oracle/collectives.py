@@ -69,7 +69,7 @@ def fold(xs, op, dtype, order):
 def direct_allreduce(xs, op, dtype):
     """Direct AllReduce, ascending rank order; returns N identical outputs."""
     n = len(xs)
-    y = R.narrow(fold(xs, op, dtype, list(range(n))), dtype)
+    y = R.narrow(R.finalize(op, fold(xs, op, dtype, list(range(n))), n), dtype)
     return [y.copy() for _ in range(n)]
 
 
@@ -84,7 +84,7 @@ def reduce_scatter(xs, op, dtype, recvcount):
     for x in xs:
         if np.asarray(x).size != n * recvcount:
             raise TypeError("input tensor must be the same size as output size times world size")
-    full = R.narrow(fold(xs, op, dtype, list(range(n))), dtype)
+    full = R.narrow(R.finalize(op, fold(xs, op, dtype, list(range(n))), n), dtype)
     return [full[r * recvcount:(r + 1) * recvcount].copy() for r in range(n)]
 
 

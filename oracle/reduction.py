@@ -2,11 +2,18 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring for who may import it).
 
-[PRIMS] §二.1 lists the reduction operators sum, max, min, prod (and avg).
+[PRIMS] §二.1 lists the reduction operators sum, max, min, prod and avg.
 [DECOMP] §等价成立的条件, condition three, fixes two identities: 0 for SUM
 and "negative infinity or the dtype's minimum" for MAX, never a mechanical 0.
 The identities of PROD (1) and MIN (+inf / dtype maximum) are not printed on
 the pages; they are the plain readings of "identity of the reduction".
+
+AVG is a SUM fold followed by one division by N when the final result is
+stored (the postOp flag on the last reduce of [DECOMP] §源码三 / §源码四).
+Reading taken for its details: float32 and bf16 divide the float32 sum by
+N with one correctly rounded binary32 division; integers divide the
+(wrapped) sum by N truncating toward zero, as C's integer division does.
+Its padding identity is SUM's, 0.
 
 Representation
 --------------
@@ -26,7 +33,7 @@ tie, which only matters for +0 / -0).  NaN inputs are out of scope.
 import numpy as np
 
 DTYPES = ("int32", "int64", "float32", "bfloat16")
-OPS = ("sum", "prod", "max", "min")
+OPS = ("sum", "prod", "max", "min", "avg")
 
 # NumPy dtype that holds one stored element.
 STORAGE = {
@@ -55,7 +62,7 @@ def identity(op, dtype):
     """Identity of ⊕ in the accumulator type ([DECOMP] condition three)."""
     _check(op, dtype)
     acc = ACCUM[dtype]
-    if op == "sum":
+    if op in ("sum", "avg"):
         return acc.type(0)
     if op == "prod":
         return acc.type(1)
@@ -112,7 +119,7 @@ def combine(op, a, b):
     wrap (NumPy array arithmetic is modular); float32 SUM / PROD are single
     IEEE binary32 operations.
     """
-    if op == "sum":
+    if op in ("sum", "avg"):
         return np.add(a, b, dtype=a.dtype)
     if op == "prod":
         return np.multiply(a, b, dtype=a.dtype)
@@ -121,6 +128,20 @@ def combine(op, a, b):
     if op == "min":
         return np.where(b < a, b, a)
     raise ValueError(f"unknown op {op!r}")
+
+
+def finalize(op, acc, nranks):
+    """The post-operation applied once to a completed reduction: AVG divides
+    by N (float: one binary32 division; integer: truncation toward zero);
+    every other op leaves the value as it is."""
+    if op != "avg":
+        return acc
+    acc = np.asarray(acc)
+    if acc.dtype.kind == "f":
+        return np.divide(acc, acc.dtype.type(nranks), dtype=acc.dtype)
+    q = acc // nranks                      # floor division ...
+    rem = acc - q * nranks
+    return np.where((rem != 0) & (acc < 0), q + 1, q).astype(acc.dtype)  # ... turned toward zero
 
 
 def fp64_reference(xs, dtype):

@@ -128,7 +128,12 @@ def ring_allreduce(xs, op, dtype, record=False):
     padded = pad_identity(xs, op, dtype, n * q)
     bufs = [R.widen(x, dtype) for x in padded]
     rs_states = _rs_phase(bufs, op, q, record)
-    stored = [R.narrow(b, dtype) for b in bufs]
+    stored = []
+    for owner, b in enumerate(bufs):
+        b = b.copy()
+        sl = _chunk(q, ring_owner(n, owner))
+        b[sl] = R.finalize(op, b[sl], n)   # the completed chunk gets the post-operation
+        stored.append(R.narrow(b, dtype))
     ag_states = _ag_phase(stored, q, 1, record)
     outs = [b[:m].copy() for b in stored]
     if record:
@@ -152,7 +157,7 @@ def ring_reduce_scatter(xs, op, dtype, recvcount, record=False):
     shards = [None] * n
     for owner in range(n):
         c = ring_owner(n, owner)
-        shards[c] = R.narrow(bufs[owner][_chunk(q, c)], dtype)
+        shards[c] = R.narrow(R.finalize(op, bufs[owner][_chunk(q, c)], n), dtype)
     if record:
         return shards, states
     return shards

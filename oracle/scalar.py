@@ -84,7 +84,7 @@ def f32_to_bf16(x):
 
 
 def identity(op, dtype):
-    if op == "sum":
+    if op in ("sum", "avg"):
         return 0.0 if dtype in ("float32", "bfloat16") else 0
     if op == "prod":
         return 1.0 if dtype in ("float32", "bfloat16") else 1
@@ -109,10 +109,21 @@ def combine(op, a, b, dtype):
     if op == "min":
         return b if b < a else a
     if dtype in ("int32", "int64"):
-        v = a + b if op == "sum" else a * b
+        v = a * b if op == "prod" else a + b
         return _wrap(v, _BITS[dtype])
-    v = a + b if op == "sum" else a * b
+    v = a * b if op == "prod" else a + b
     return f32(v)
+
+
+def finalize(op, v, n, dtype):
+    """AVG: divide the completed sum by N once (binary32 division, or integer
+    division truncating toward zero); other ops unchanged."""
+    if op != "avg":
+        return v
+    if dtype in ("int32", "int64"):
+        q = abs(v) // n
+        return q if v >= 0 else -q
+    return f32(v / n)
 
 
 def allreduce_direct(xs, op, dtype):
@@ -123,7 +134,7 @@ def allreduce_direct(xs, op, dtype):
         acc = widen(xs[0][i], dtype)
         for s in range(1, n):
             acc = combine(op, acc, widen(xs[s][i], dtype), dtype)
-        y.append(narrow(acc, dtype))
+        y.append(narrow(finalize(op, acc, n, dtype), dtype))
     return [list(y) for _ in range(n)]
 
 
@@ -140,7 +151,7 @@ def allreduce_rs_ag(xs, op, dtype):
             acc = widen(padded[0][r * q + j], dtype)
             for s in range(1, n):
                 acc = combine(op, acc, widen(padded[s][r * q + j], dtype), dtype)
-            z.append(narrow(acc, dtype))
+            z.append(narrow(finalize(op, acc, n, dtype), dtype))
         shards.append(z)
     gathered = [v for z in shards for v in z][:m]
     return [list(gathered) for _ in range(n)]
@@ -156,5 +167,5 @@ def allreduce_ring(xs, op, dtype):
         acc = widen(xs[c][i], dtype)
         for k in range(1, n):
             acc = combine(op, acc, widen(xs[(c + k) % n][i], dtype), dtype)
-        y.append(narrow(acc, dtype))
+        y.append(narrow(finalize(op, acc, n, dtype), dtype))
     return [list(y) for _ in range(n)]
