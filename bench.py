@@ -172,6 +172,7 @@ def main():
         counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype)
         return
 
+    send_elem_size = send[0].element_size()
     bytes_rs = cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct")
     bytes_ag = cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")
     bytes_step = bytes_rs + bytes_ag
@@ -228,6 +229,23 @@ def main():
         torch.cuda.empty_cache()
         secondary.update(run_many_ranks(cs, torch, stream, args.secondary_iters))
 
+    # Modeled context only (not a measurement, not a target): the pages'
+    # α-β model of the same collective between N real ranks on their two
+    # example links.
+    modeled = {}
+    for label, alpha_us, beta_gbps in (("ib_hdr_alpha10us_beta25GBps", 10.0, 25.0),
+                                       ("alpha5us_beta300GBps", 5.0, 300.0)):
+        for algo in ("ring", "tree"):
+            modeled[f"{label}_{algo}"] = cs.ccl_sim_model_estimate("all_reduce", algo, n, m * send_elem_size,
+                                                                  alpha_us, beta_gbps)
+
+    lifetimes = None
+    if not args.no_secondary:
+        from collective_reduction_amd import lifetime as LT
+        lifetimes = {mode: LT.measure(mode, 4, 64 << 20, "float32", "direct") for mode in LT.MODES}
+        log("lifetimes (MiB per rank, steady/peak): " + ", ".join(
+            f"{k} {v['steady'] / 2**20:.0f}/{v['peak'] / 2**20:.0f}" for k, v in lifetimes.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -256,6 +274,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "secondary": secondary,
+        "modeled_context": modeled,
+        "lifetimes_256MiB_per_rank_world4": lifetimes,
         "cpu_baseline": cpu,
         "device": dev_name,
         "kernel_source_digest": kernel_source_digest(),
@@ -285,7 +305,7 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
     HIP events over `iters` calls after one warm-up call."""
     res = {}
     ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
-                               for s in ("ring_stepwise", "ring_persistent")])
+                               for s in ("ring_stepwise", "ring_persistent", "recursive")])
 
     def timed(name, fn, nbytes):
         try:
@@ -307,12 +327,12 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
             log(f"{name}: {e}")
 
     ab = cs.ccl_sim_algorithmic_bytes
-    for sched in ("ring_stepwise", "ring_persistent"):
+    for sched in ("ring_stepwise", "ring_persistent", "recursive"):
         timed(f"rs_ag_{sched}", lambda s=sched: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
             ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched))
-    for sched in ("direct", "ring_stepwise", "ring_persistent"):
+    for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive"):
         timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
             send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
     timed("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
@@ -350,7 +370,7 @@ def run_many_ranks(cs, torch, stream, iters):
         recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
         shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
         ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
-                                   for s in ("direct", "ring_stepwise", "ring_persistent")])
+                                   for s in ("direct", "ring_stepwise", "ring_persistent", "recursive")])
         torch.cuda.synchronize()
 
         def timed(key, fn, nbytes):
@@ -367,7 +387,7 @@ def run_many_ranks(cs, torch, stream, iters):
                                     "frac_of_peak": nbytes / (st["median_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, **st}
             log(f"{key}_{name}: {st['median_ms']:.3f} ms, {res[f'{key}_{name}']['gbs']:.0f} GB/s")
 
-        for sched in ("direct", "ring_stepwise", "ring_persistent"):
+        for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive"):
             timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(send, recv, m, schedule=s, workspace=ws,
                                                                             stream=stream),
                   ab("allreduce", n, m, dtype, sched))

@@ -21,6 +21,9 @@ _BINDING_NAMES = (
     "ccl_sim_launch_count",
     "ccl_sim_result_string",
     "ccl_sim_version",
+    "ccl_sim_model_estimate",
+    "ccl_sim_busbw_factor",
+    "ccl_sim_recursive_route",
     "Workspace",
     "CclSimError",
 )

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libccl_sim.so")
-SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "model.cpp"), os.path.join(CSRC, "kernels.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.

@@ -47,8 +47,8 @@ if len(_hip_runtimes_mapped()) > 1:
 # enums (include/ccl_sim.h)
 SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, INSUFFICIENT_WORKSPACE, HIP_ERROR, CAPACITY_MISMATCH = range(6)
 DTYPES = {"int32": 0, "int64": 1, "float32": 2, "bfloat16": 3}
-OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3}
-SCHEDULES = {"direct": 0, "ring_stepwise": 1, "ring_persistent": 2}
+OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
+SCHEDULES = {"direct": 0, "ring_stepwise": 1, "ring_persistent": 2, "recursive": 3}
 COLLS = {"reduce_scatter": 0, "all_gather": 1, "allreduce": 2}
 INLINE_RANKS = 64
 MAX_RANKS = 1024
@@ -87,13 +87,36 @@ _ring_owner = _sig("ccl_sim_ring_owner", ctypes.c_int, [ctypes.c_int, ctypes.c_i
 _ring_route = _sig("ccl_sim_ring_route", ctypes.c_int,
                    [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                     ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)])
+_recursive_route = _sig("ccl_sim_recursive_route", ctypes.c_int,
+                        [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)])
 _result_string = _sig("ccl_sim_result_string", ctypes.c_char_p, [ctypes.c_int])
 _last_error = _sig("ccl_sim_last_error", ctypes.c_char_p, [])
 _version = _sig("ccl_sim_version", ctypes.c_int, [])
 
+
+class _LinkParams(ctypes.Structure):
+    _fields_ = [("alpha_s", ctypes.c_double), ("beta_bytes_per_s", ctypes.c_double), ("ranks_per_node", ctypes.c_int),
+                ("alpha_intra_s", ctypes.c_double), ("beta_intra_bytes_per_s", ctypes.c_double)]
+
+
+class _Estimate(ctypes.Structure):
+    _fields_ = [("time_s", ctypes.c_double), ("latency_s", ctypes.c_double), ("bandwidth_s", ctypes.c_double),
+                ("latency_fraction", ctypes.c_double), ("algbw_gbps", ctypes.c_double),
+                ("busbw_gbps", ctypes.c_double), ("steps", ctypes.c_double)]
+
+
+_model_estimate = _sig("ccl_sim_model_estimate", ctypes.c_int,
+                       [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.POINTER(_LinkParams),
+                        ctypes.POINTER(_Estimate)])
+_busbw_factor = _sig("ccl_sim_busbw_factor", ctypes.c_double, [ctypes.c_int, ctypes.c_int])
+MODEL_COLLS = {"all_reduce": 0, "all_gather": 1, "reduce_scatter": 2, "all_to_all": 3, "broadcast": 4, "reduce": 5}
+MODEL_ALGOS = {"ring": 0, "tree": 1, "2level": 2}
+
 EXPORTED = ("ccl_sim_reduce_scatter", "ccl_sim_all_gather", "ccl_sim_allreduce", "ccl_sim_pad_identity",
             "ccl_sim_workspace_size", "ccl_sim_algorithmic_bytes", "ccl_sim_launch_count", "ccl_sim_ring_owner",
-            "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version")
+            "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version",
+            "ccl_sim_model_estimate", "ccl_sim_busbw_factor", "ccl_sim_recursive_route")
 
 
 class CclSimError(RuntimeError):
@@ -258,6 +281,14 @@ def ccl_sim_ring_route(nranks, phase, step, rank):
     return s.value, r.value
 
 
+def ccl_sim_recursive_route(nranks, phase, step, rank):
+    """(partner, first_block, nblocks); phase 0 halving step (1-based),
+    phase 1 doubling step (0-based)."""
+    p, f, nb = ctypes.c_int(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_recursive_route(nranks, phase, step, rank, ctypes.byref(p), ctypes.byref(f), ctypes.byref(nb)))
+    return p.value, f.value, nb.value
+
+
 def ccl_sim_result_string(code):
     return _result_string(code).decode()
 
@@ -268,6 +299,23 @@ def ccl_sim_last_error():
 
 def ccl_sim_version():
     return _version()
+
+
+def ccl_sim_model_estimate(coll, algo, nranks, size_bytes, alpha_us=10.0, beta_gbps=25.0, ranks_per_node=8,
+                           alpha_intra_us=3.0, beta_intra_gbps=200.0):
+    """α-β model of a collective on a network (see ccl_sim.h); returns a dict
+    with time_s, latency_s, bandwidth_s, latency_fraction, algbw_gbps,
+    busbw_gbps and steps.  Bandwidths are 10^9 bytes per second."""
+    link = _LinkParams(alpha_us * 1e-6, beta_gbps * 1e9, ranks_per_node, alpha_intra_us * 1e-6,
+                       beta_intra_gbps * 1e9)
+    est = _Estimate()
+    _check(_model_estimate(_enum(MODEL_COLLS, coll, "coll"), _enum(MODEL_ALGOS, algo, "algo"), nranks,
+                           float(size_bytes), ctypes.byref(link), ctypes.byref(est)))
+    return {name: getattr(est, name) for name, _ in _Estimate._fields_}
+
+
+def ccl_sim_busbw_factor(coll, nranks):
+    return _busbw_factor(_enum(MODEL_COLLS, coll, "coll"), nranks)
 
 
 class Workspace:

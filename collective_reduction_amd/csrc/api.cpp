@@ -37,8 +37,14 @@ ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
 }
 
 bool valid_dtype(int d) { return d >= CCL_SIM_INT32 && d <= CCL_SIM_BFLOAT16; }
-bool valid_op(int o) { return o >= CCL_SIM_SUM && o <= CCL_SIM_MIN; }
-bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RING_PERSISTENT; }
+bool valid_op(int o) { return o >= CCL_SIM_SUM && o <= CCL_SIM_AVG; }
+bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RECURSIVE; }
+bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+int log2i(int n) {
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  return k;
+}
 bool valid_coll(int c) { return c >= CCL_SIM_COLL_REDUCE_SCATTER && c <= CCL_SIM_COLL_ALLREDUCE; }
 
 constexpr size_t kAlign = 256;
@@ -71,10 +77,18 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
     l.recv_tab = off + tab;
     off += 2 * tab;
   }
-  if (sched != CCL_SIM_DIRECT && coll != CCL_SIM_COLL_ALL_GATHER && nranks >= 3) {
+  const bool ring = sched == CCL_SIM_RING_STEPWISE || sched == CCL_SIM_RING_PERSISTENT;
+  const bool halving = sched == CCL_SIM_RECURSIVE;
+  if ((ring && nranks >= 3) || (halving && nranks >= 4)) {
+    if (coll == CCL_SIM_COLL_ALL_GATHER) {
+      l.total = off;
+      return l;
+    }
     const uint64_t q = shard_len(m, nranks);
+    // ring: [2][N][q] partials; recursive halving: [N][(N/2)·q] per-rank halves
+    const uint64_t per_q = ring ? uint64_t(2) * uint64_t(nranks) : uint64_t(nranks) * uint64_t(nranks / 2);
     uint64_t bytes = 0;
-    if (__builtin_mul_overflow(q, uint64_t(2) * uint64_t(nranks) * accum_size(dtype), &bytes) ||
+    if (__builtin_mul_overflow(q, per_q * accum_size(dtype), &bytes) ||
         bytes > SIZE_MAX - off - kAlign) {
       l.ok = false;
       return l;
@@ -187,6 +201,8 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", dtype);
   if (coll != CCL_SIM_COLL_ALL_GATHER && !valid_op(op)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid op %d", op);
   if (!valid_sched(schedule)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid schedule %d", schedule);
+  if (schedule == CCL_SIM_RECURSIVE && !pow2(nranks))
+    return fail(CCL_SIM_UNSUPPORTED, "the recursive halving schedule needs a power-of-two nranks (got %d)", nranks);
   const size_t es = elem_size(dtype);
 
   // Counts ([DECOMP] §源码一 count rules; §Contract 实验四 capacity check).
@@ -297,6 +313,8 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     e = run_direct(c);
   } else if (sched == CCL_SIM_RING_STEPWISE) {
     e = run_ring_stepwise(c);
+  } else if (sched == CCL_SIM_RECURSIVE) {
+    e = run_recursive(c);
   } else {
     bool unsupported = false;
     PersistentPlan plan;
@@ -427,6 +445,21 @@ uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count
     return (n + 1) * m * s;
   }
   if (coll == CCL_SIM_COLL_ALL_GATHER) return 2 * n * m * s;
+  if (sched == CCL_SIM_RECURSIVE) {
+    if (!pow2(nranks)) return 0;
+    // halving step j: every position is reduced by N/2^j ranks, each reading
+    // two partials (the inputs at step 1) and writing one (the output at the
+    // last step)
+    const int k = log2i(nranks);
+    uint64_t bytes = 0;
+    for (int j = 1; j <= k; ++j) {
+      const uint64_t in = (j == 1) ? 2 * s : 2 * a;
+      const uint64_t out = (j == k) ? s : a;
+      bytes += (n >> j) * m * (in + out);
+    }
+    if (coll == CCL_SIM_COLL_ALLREDUCE) bytes += 2 * (n - 1) * m * s;
+    return bytes;
+  }
   // ReduceScatter phase: per step every position reads the incoming partial
   // (stored type at the first step) and the own element, and writes the new
   // partial (stored type at the last step).
@@ -446,6 +479,13 @@ int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_
   if (count == 0) return 0;
   const int sched = effective_schedule(nranks, schedule);
   if (sched == CCL_SIM_DIRECT || sched == CCL_SIM_RING_PERSISTENT) return 1;
+  if (sched == CCL_SIM_RECURSIVE) {
+    if (!pow2(nranks)) return -1;
+    const int k = log2i(nranks);
+    if (coll == CCL_SIM_COLL_ALLREDUCE) return 2 * k;
+    if (coll == CCL_SIM_COLL_REDUCE_SCATTER) return k;
+    return in_place ? k : k + 1;
+  }
   if (coll == CCL_SIM_COLL_ALLREDUCE) return 2 * (nranks - 1);
   if (coll == CCL_SIM_COLL_REDUCE_SCATTER) return nranks - 1;
   return in_place ? nranks - 1 : nranks;
@@ -465,6 +505,29 @@ ccl_sim_result_t ccl_sim_ring_route(int nranks, int phase, int step, int rank, i
   *send_chunk = mod(rank + owner - step);
   *recv_chunk = mod(rank + owner - 1 - step);
   return CCL_SIM_SUCCESS;
+}
+
+ccl_sim_result_t ccl_sim_recursive_route(int nranks, int phase, int step, int rank, int* partner,
+                                         size_t* first_block, size_t* nblocks) {
+  if (!pow2(nranks) || rank < 0 || rank >= nranks || partner == nullptr || first_block == nullptr ||
+      nblocks == nullptr)
+    return CCL_SIM_INVALID_ARGUMENT;
+  const int k = log2i(nranks);
+  if (phase == 0 && step >= 1 && step <= k) {
+    const int d = nranks >> step;
+    *partner = rank ^ d;
+    *first_block = size_t(rank & ((nranks - 1) & ~(d - 1)));
+    *nblocks = size_t(d);
+    return CCL_SIM_SUCCESS;
+  }
+  if (phase == 1 && step >= 0 && step < k) {
+    const int p = rank ^ (1 << step);
+    *partner = p;
+    *first_block = size_t((p >> step) << step);
+    *nblocks = size_t(1) << step;
+    return CCL_SIM_SUCCESS;
+  }
+  return CCL_SIM_INVALID_ARGUMENT;
 }
 
 const char* ccl_sim_result_string(ccl_sim_result_t result) {

@@ -18,8 +18,10 @@ constexpr int kInlineRanks = 64;  // rank pointers passed in the kernel argument
 #endif
 constexpr int kRankBatch = CCL_SIM_RANK_BATCH;
 
-// The reduction operators of [PRIMS] §二.1.
-enum Op : int { kSum = 0, kProd = 1, kMax = 2, kMin = 3 };
+// The reduction operators of [PRIMS] §二.1.  AVG combines as SUM and divides
+// the completed result by N once, when it is stored (the postOp of the last
+// reduce in [DECOMP] §源码三 / §源码四).
+enum Op : int { kSum = 0, kProd = 1, kMax = 2, kMin = 3, kAvg = 4 };
 
 // ---------------------------------------------------------------------------
 // Element types.  S = stored element, A = accumulator.  Integer SUM / PROD
@@ -89,7 +91,7 @@ struct BF16 {
 template <class T, int OP>
 __device__ inline typename T::A identity() {
   using A = typename T::A;
-  if constexpr (OP == kSum) return A(0);
+  if constexpr (OP == kSum || OP == kAvg) return A(0);
   else if constexpr (OP == kProd) return A(1);
   else if constexpr (OP == kMax) return T::lowest();
   else return T::highest();
@@ -101,7 +103,7 @@ __device__ inline typename T::A identity() {
 template <class T, int OP>
 __device__ inline typename T::A combine(typename T::A a, typename T::A b) {
   using A = typename T::A;
-  if constexpr (OP == kSum) {
+  if constexpr (OP == kSum || OP == kAvg) {
     if constexpr (T::kFloat) return a + b;
     else return static_cast<A>(static_cast<typename T::U>(a) + static_cast<typename T::U>(b));
   } else if constexpr (OP == kProd) {
@@ -111,6 +113,20 @@ __device__ inline typename T::A combine(typename T::A a, typename T::A b) {
     return (b > a) ? b : a;
   } else {
     return (b < a) ? b : a;
+  }
+}
+
+// The post-operation on a completed reduction: AVG divides by N (one
+// correctly rounded float32 division, or integer division truncating toward
+// zero); every other op returns the value unchanged.
+template <class T, int OP>
+__device__ inline typename T::A finalize(typename T::A v, int nranks) {
+  using A = typename T::A;
+  if constexpr (OP == kAvg) {
+    if constexpr (T::kFloat) return v / static_cast<A>(nranks);
+    else return v / static_cast<A>(nranks);
+  } else {
+    return v;
   }
 }
 

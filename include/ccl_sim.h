@@ -68,6 +68,8 @@
  *            outputs are bit-identical.  bf16 is accumulated in float32 and
  *            rounded to nearest even once, when a result is stored.
  *            MAX / MIN keep the running partial on ties.
+ *            CCL_SIM_RECURSIVE reduces each block as the butterfly tree of
+ *            its halving steps.
  * Threads.   The library holds no mutable global state except a cached
  *            per-device compute-unit count and a thread-local error
  *            message; calls with distinct workspaces may run concurrently.
@@ -102,12 +104,17 @@ typedef enum {
   CCL_SIM_BFLOAT16 = 3
 } ccl_sim_dtype_t;
 
-/* The reduction operators of [PRIMS] §二.1 (avg is not provided). */
+/* The reduction operators of [PRIMS] §二.1.  AVG combines as SUM and divides
+ * the completed result by nranks once, when it is stored (the postOp of
+ * [DECOMP] §源码三): one correctly rounded float32 division for float32 and
+ * bf16, integer division truncating toward zero for int32 / int64.  Its
+ * padding identity is 0. */
 typedef enum {
   CCL_SIM_SUM = 0,
   CCL_SIM_PROD = 1,
   CCL_SIM_MAX = 2,
-  CCL_SIM_MIN = 3
+  CCL_SIM_MIN = 3,
+  CCL_SIM_AVG = 4
 } ccl_sim_op_t;
 
 typedef enum {
@@ -117,7 +124,14 @@ typedef enum {
   CCL_SIM_RING_STEPWISE = 1,
   /* The same ring steps inside one cooperative kernel, a grid-wide barrier
    * between steps. */
-  CCL_SIM_RING_PERSISTENT = 2
+  CCL_SIM_RING_PERSISTENT = 2,
+  /* Recursive-halving ReduceScatter and recursive-doubling AllGather
+   * ([RS-PAGE] §Recursive Halving ReduceScatter): log2 N steps per phase, one
+   * launch per step; nranks must be a power of two (else
+   * CCL_SIM_UNSUPPORTED).  Block b is reduced as a butterfly: at halving
+   * step j ranks i and i XOR N/2^j combine (lower rank's partial) ⊕ (upper
+   * rank's partial). */
+  CCL_SIM_RECURSIVE = 3
 } ccl_sim_schedule_t;
 
 typedef enum {
@@ -183,8 +197,8 @@ ccl_sim_result_t ccl_sim_allreduce(const void* const* sendbufs, void* const* rec
  * Identity padding ([DECOMP] §等价成立的条件, condition three):
  *     dsts[r][i] = srcs[r][i]     for i < count,
  *     dsts[r][i] = identity(op)   for count <= i < padded_count,
- * with identity 0 (SUM), 1 (PROD), -inf / INT_MIN (MAX), +inf / INT_MAX
- * (MIN) — never a mechanical zero.  srcs[r] == dsts[r] only fills the tail.
+ * with identity 0 (SUM, AVG), 1 (PROD), -inf / INT_MIN (MAX), +inf /
+ * INT_MAX (MIN) — never a mechanical zero.  srcs[r] == dsts[r] only fills the tail.
  * padded_count < count is CCL_SIM_INVALID_ARGUMENT.  No workspace needed.
  */
 ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts, int nranks, size_t count,
@@ -210,6 +224,10 @@ size_t ccl_sim_workspace_size(ccl_sim_coll_t coll, int nranks, size_t count, ccl
  * movement must read or write, counted once per access (the numerator of
  * the effective bandwidth).  s = element size, a = accumulator size:
  *   DIRECT  ReduceScatter (N+1)·M·s    AllGather (N+1)·M·s    AllReduce 2N·M·s
+ *   RECURSIVE  halving step j: each position is reduced by N/2^j ranks,
+ *           each reading two partials (the inputs at step 1) and writing one
+ *           (the output at the last step): 3(N-1)·M·s for 4- and 8-byte
+ *           types; AllGather and the AllReduce's gather phase as the ring.
  *   ring    ReduceScatter: per step, each of the M positions reads the
  *           incoming partial and the rank's own element and writes the new
  *           partial; the first step's incoming partial and the last step's
@@ -248,6 +266,81 @@ int ccl_sim_ring_owner(int nranks, int rank);
  */
 ccl_sim_result_t ccl_sim_ring_route(int nranks, int phase, int step, int rank, int* send_chunk,
                                     int* recv_chunk);
+
+/*
+ * α-β (Hockney) cost model of a collective between N real ranks joined by
+ * links of per-step latency α and bandwidth β ([PRIMS] §四 and §五; the ring
+ * terms of [RING] §5 and [RS-PAGE] §Ring ReduceScatter).  A model, not a
+ * measurement: it prices the pages' algorithms on a network so that a bench
+ * row can carry modeled context.  T = steps·α + bytes_per_rank / β:
+ *   ring        AllReduce 2(N-1) steps, 2(N-1)/N·S bytes; AllGather,
+ *               ReduceScatter, all_to_all N-1 steps, (N-1)/N·S bytes;
+ *               broadcast, reduce N-1 steps, S bytes (pipelined chain)
+ *               ([PRIMS] §五.4);
+ *   double tree AllReduce only: 2·ceil(log2 N) steps, 2S bytes ([PRIMS] §六);
+ *   two-level   AllReduce only: intra-node ReduceScatter over ppn ranks,
+ *               inter-node ring AllReduce of S/ppn over N/ppn nodes,
+ *               intra-node AllGather ([PRIMS] §八).
+ * algbw = S / T and busbw = algbw · factor, factor 2(N-1)/N for AllReduce,
+ * (N-1)/N for AllGather, ReduceScatter and all_to_all, 1 for broadcast and
+ * reduce ([PRIMS] §七, in 10^9 bytes per second).  S is in bytes as the
+ * pages define it per primitive ([PRIMS] §二.1).
+ */
+typedef enum {
+  CCL_SIM_MODEL_ALLREDUCE = 0,
+  CCL_SIM_MODEL_ALL_GATHER = 1,
+  CCL_SIM_MODEL_REDUCE_SCATTER = 2,
+  CCL_SIM_MODEL_ALL_TO_ALL = 3,
+  CCL_SIM_MODEL_BROADCAST = 4,
+  CCL_SIM_MODEL_REDUCE = 5
+} ccl_sim_model_coll_t;
+
+typedef enum {
+  CCL_SIM_ALGO_RING = 0,
+  CCL_SIM_ALGO_DOUBLE_TREE = 1,
+  CCL_SIM_ALGO_TWO_LEVEL = 2
+} ccl_sim_model_algo_t;
+
+typedef struct {
+  double alpha_s;                 /* per-step latency, seconds (inter-node for two-level) */
+  double beta_bytes_per_s;        /* link bandwidth, bytes per second (inter-node for two-level) */
+  int ranks_per_node;             /* two-level only: ppn, must divide nranks */
+  double alpha_intra_s;           /* two-level only */
+  double beta_intra_bytes_per_s;  /* two-level only */
+} ccl_sim_link_params_t;
+
+typedef struct {
+  double time_s;            /* latency_s + bandwidth_s */
+  double latency_s;         /* steps · alpha */
+  double bandwidth_s;       /* bytes_per_rank / beta (summed over phases for two-level) */
+  double latency_fraction;  /* latency_s / time_s (0 when time_s is 0) */
+  double algbw_gbps;        /* S / time_s in 10^9 B/s (0 when time_s is 0) */
+  double busbw_gbps;        /* algbw · ccl_sim_busbw_factor */
+  double steps;             /* communication steps on the critical path */
+} ccl_sim_model_estimate_t;
+
+/* Fills *out.  CCL_SIM_INVALID_ARGUMENT for nranks < 1, negative sizes or
+ * latencies, non-positive bandwidths, NULL pointers or ppn not dividing
+ * nranks; CCL_SIM_UNSUPPORTED for a tree or two-level model of anything but
+ * AllReduce. */
+ccl_sim_result_t ccl_sim_model_estimate(ccl_sim_model_coll_t coll, ccl_sim_model_algo_t algo, int nranks,
+                                        double size_bytes, const ccl_sim_link_params_t* link,
+                                        ccl_sim_model_estimate_t* out);
+
+/* busbw / algbw for the collective at nranks ([PRIMS] §七); -1 if invalid. */
+double ccl_sim_busbw_factor(ccl_sim_model_coll_t coll, int nranks);
+
+/*
+ * Recursive halving / doubling routing ([RS-PAGE] §Recursive Halving
+ * ReduceScatter; N a power of two).  phase 0 = halving step `step` in
+ * [1, log2 N]: *partner = rank XOR N/2^step, and [*first_block,
+ * *first_block + *nblocks) are the blocks of q elements rank keeps and
+ * reduces at that step.  phase 1 = doubling step `step` in [0, log2 N):
+ * *partner = rank XOR 2^step, and the block range is what rank receives
+ * from it.  CCL_SIM_INVALID_ARGUMENT when out of range.
+ */
+ccl_sim_result_t ccl_sim_recursive_route(int nranks, int phase, int step, int rank, int* partner,
+                                         size_t* first_block, size_t* nblocks);
 
 const char* ccl_sim_result_string(ccl_sim_result_t result);
 

@@ -9,7 +9,11 @@ from collective_reduction_amd import inputs as I
 
 TORCH = {"int32": torch.int32, "int64": torch.int64, "float32": torch.float32, "bfloat16": torch.bfloat16}
 NP = {"int32": np.int32, "int64": np.int64, "float32": np.float32, "bfloat16": np.uint16}
-SCHEDULES = ("direct", "ring_stepwise", "ring_persistent")
+SCHEDULES = ("direct", "ring_stepwise", "ring_persistent", "recursive")
+
+
+def pow2(n):
+    return n > 0 and (n & (n - 1)) == 0
 
 
 def to_dev(x, dtype, device="cuda"):

@@ -66,6 +66,7 @@ def test_argument_validation(cs):
     s, r = fake(n, m, 4), fake(n, m, 4, base=BASE * 3)
     ar = cs.ccl_sim_allreduce
     assert code_of(ar, s, r, m, dtype="float32", op=9) == cs.INVALID_ARGUMENT
+    assert code_of(ar, s, r, m, dtype="float32", op=5) == cs.INVALID_ARGUMENT
     assert code_of(ar, s, r, m, dtype=7) == cs.INVALID_ARGUMENT
     assert code_of(ar, s, r, m, dtype="float32", schedule=5) == cs.INVALID_ARGUMENT
     assert code_of(ar, [], [], m, dtype="float32") == cs.INVALID_ARGUMENT
@@ -186,6 +187,41 @@ def test_ring_routing_matches_the_n4_table(cs, golden):
     assert cs.ccl_sim_ring_owner(4, 4) == -1
     with pytest.raises(Exception):
         cs.ccl_sim_ring_route(4, 0, 3, 0)
+
+
+def test_recursive_routing_matches_the_pair_table(cs, golden):
+    g = golden("recursive_halving_n8.json")
+    n = g["nranks"]
+    for j, pairs in enumerate(g["pairs"], start=1):
+        for a, b in pairs:
+            pa, fa, na = cs.ccl_sim_recursive_route(n, 0, j, a)
+            pb, fb, nb = cs.ccl_sim_recursive_route(n, 0, j, b)
+            assert (pa, pb) == (b, a)
+            assert na == nb == g["data_per_node_after"][j - 1] * n
+            assert fa + na == fb  # the lower rank keeps the lower half
+    for i in range(n):
+        assert cs.ccl_sim_recursive_route(n, 0, 3, i)[1:] == (i, 1)
+    # doubling: rank 5 gets block 4 from rank 4, then blocks 6-7, then 0-3
+    assert [cs.ccl_sim_recursive_route(n, 1, t, 5) for t in range(3)] == [(4, 4, 1), (7, 6, 2), (1, 0, 4)]
+    with pytest.raises(Exception):
+        cs.ccl_sim_recursive_route(6, 0, 1, 0)
+
+
+def test_recursive_planning(cs):
+    ws, ab, lc = cs.ccl_sim_workspace_size, cs.ccl_sim_algorithmic_bytes, cs.ccl_sim_launch_count
+    n, m = 8, 1 << 28
+    assert ws("allreduce", n, m, "float32", "recursive") == n * (n // 2) * (m // n) * 4
+    assert ws("allreduce", 2, 1000, "float32", "recursive") == 0
+    assert ws("all_gather", 8, 1000, "float32", "recursive") == 0
+    assert ab("reduce_scatter", n, m, "float32", "recursive") == 3 * (n - 1) * m * 4
+    assert ab("allreduce", n, m, "float32", "recursive") == 5 * (n - 1) * m * 4
+    assert ab("all_gather", n, m, "float32", "recursive") == 2 * n * m * 4
+    assert lc("allreduce", 8, 100, "recursive") == 6
+    assert lc("reduce_scatter", 256, 100, "recursive") == 8
+    assert lc("all_gather", 16, 100, "recursive") == 5
+    assert lc("allreduce", 6, 100, "recursive") == -1
+    s, r = fake(6, 60, 4), fake(6, 60, 4, base=BASE * 3)
+    assert code_of(cs.ccl_sim_allreduce, s, r, 60, dtype="float32", schedule="recursive") == cs.UNSUPPORTED
 
 
 def test_result_strings(cs):

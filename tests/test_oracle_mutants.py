@@ -45,6 +45,7 @@ PINS = [
     lambda: P.test_fp32_ring_fold_matches_chunk_order(),
     lambda: P.test_bf16_rounding_cases(),
     lambda: P.test_gradient_like_256_ranks_tolerance(),
+    lambda: P.test_avg_is_the_sum_divided_once(),
 ]
 
 
@@ -103,9 +104,20 @@ def _owner_same_rank(nranks, rank):
     return rank
 
 
+def _finalize_floor(op, acc, nranks):
+    if op == "avg" and np.asarray(acc).dtype.kind == "i":
+        return (np.asarray(acc) // nranks).astype(np.asarray(acc).dtype)
+    return _ORIG_FINALIZE(op, acc, nranks)
+
+
+def _finalize_by_n_minus_1(op, acc, nranks):
+    return _ORIG_FINALIZE(op, acc, nranks - 1 if nranks > 1 else 1)
+
+
 _ORIG_FOLD = C.fold
 _ORIG_GATHER = C.all_gather
 _ORIG_COMBINE = R.combine
+_ORIG_FINALIZE = R.finalize
 
 MUTANTS = {
     "fold in descending rank order": (C, "fold", _fold_descending),
@@ -118,6 +130,8 @@ MUTANTS = {
     "incoming partial is the right operand": (R, "combine", _combine_right_operand),
     "bf16 rounding truncates": (R, "bf16_round_bits", _round_truncate),
     "ring owner is the rank itself": (G, "ring_owner", _owner_same_rank),
+    "integer AVG rounds toward minus infinity": (R, "finalize", _finalize_floor),
+    "AVG divides by N-1": (R, "finalize", _finalize_by_n_minus_1),
 }
 
 

@@ -56,6 +56,9 @@ def test_worked_example_all_routes(golden):
             assert y == g["allreduce"]
     # the page's independent formula, 600 + 4i
     assert expect.tolist() == [600 + 4 * i for i in range(m)]
+    # AVG divides the same sums by the world size: 150 + i
+    for route in (C.direct_allreduce, C.allreduce_via_rs_ag, G.ring_allreduce):
+        assert route(xs, "avg", "int64")[0].tolist() == [150 + i for i in range(m)]
 
 
 def test_worked_example_negatives_differ_everywhere(golden):
@@ -273,6 +276,12 @@ def _wrap(v, bits):
     return v - (1 << bits) if v >> (bits - 1) else v
 
 
+def _trunc_div(v, n):
+    """Integer division rounding toward zero (the AVG post-operation)."""
+    q = abs(v) // n
+    return q if v >= 0 else -q
+
+
 ROUTES = {
     "direct": lambda xs, op, dt: C.direct_allreduce(xs, op, dt),
     "rs_ag": lambda xs, op, dt: C.allreduce_via_rs_ag(xs, op, dt),
@@ -295,6 +304,7 @@ def test_closed_forms(dtype, n, m, a):
     xs = affine(n, m, a, dtype)
     want = {
         "sum": [_wrap(a * n * (n - 1) // 2 + n * i, bits) for i in range(m)],
+        "avg": [_trunc_div(_wrap(a * n * (n - 1) // 2 + n * i, bits), n) for i in range(m)],
         "max": [a * (n - 1) + i for i in range(m)],
         "min": list(range(m)),
         "prod": [_wrap(math.prod(a * r + i for r in range(n)), bits) for i in range(m)],
@@ -317,6 +327,8 @@ def test_brute_force_integer_routes_agree_with_exact():
                 for op in R.OPS:
                     if op == "sum":
                         exact = [_wrap(sum(int(x[i]) for x in xs), bits) for i in range(m)]
+                    elif op == "avg":
+                        exact = [_trunc_div(_wrap(sum(int(x[i]) for x in xs), bits), n) for i in range(m)]
                     elif op == "prod":
                         exact = [_wrap(math.prod(int(x[i]) for x in xs), bits) for i in range(m)]
                     elif op == "max":
@@ -402,6 +414,24 @@ def test_fp32_ring_vs_ascending_order():
         eb = R.normalized_sum_error(b, xs, "float32")
         assert 0 < ea <= bound and 0 < eb <= bound
         assert ea <= 1e-5 * n and eb <= 1e-5 * n
+
+
+def test_avg_is_the_sum_divided_once():
+    """AVG = one correctly rounded division of the schedule's float32 sum by
+    N (checked against Python's own division of the exact binary32 sum), and
+    integer AVG truncates toward zero (-7 / 2 -> -3, not -4)."""
+    for n in (2, 3, 8):
+        xs = _f32_inputs(n, 333, 50 + n)
+        for route in (C.direct_allreduce, G.ring_allreduce):
+            s = route(xs, "sum", "float32")[0]
+            a = route(xs, "avg", "float32")[0]
+            want = np.array([np.float32(float(v) / n) for v in s], dtype=np.float32)
+            assert np.array_equal(a.view(np.uint32), want.view(np.uint32))
+    xs = [np.array([-3, 5], dtype=np.int32), np.array([-4, 2], dtype=np.int32)]
+    assert C.direct_allreduce(xs, "avg", "int32")[0].tolist() == [-3, 3]
+    xs64 = [np.array([-(2**62), 2**62], dtype=np.int64) for _ in range(3)]
+    assert C.direct_allreduce(xs64, "avg", "int64")[0].tolist() == [_trunc_div(_wrap(-3 * 2**62, 64), 3),
+                                                                     _trunc_div(_wrap(3 * 2**62, 64), 3)]
 
 
 def test_fp32_sum_matches_fsum_within_bound():
