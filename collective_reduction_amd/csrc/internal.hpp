@@ -41,7 +41,17 @@ struct PersistentPlan {
 };
 
 // Control block layout (unsigned words) at the start of the workspace.
-enum CtrlWord : int { kCtrlBarrier = 0, kCtrlAbort = 1, kCtrlWords = 64 };
+// Control block of the persistent ring (unsigned words): line 0 holds the
+// global arrival counter and the abort word, line 1 + g the arrival counter
+// of barrier group g; a line is 128 bytes.
+enum CtrlWord : int {
+  kCtrlBarrier = 0,
+  kCtrlAbort = 1,
+  kCtrlLine = 32,
+  kCtrlGroups = 8,
+  kCtrlGroup = kCtrlLine,
+  kCtrlWords = kCtrlLine * (1 + kCtrlGroups),
+};
 
 hipError_t run_direct(const Call& c);
 hipError_t run_ring_stepwise(const Call& c);

@@ -653,36 +653,60 @@ __global__ __launch_bounds__(RingPolicy::TB) void recursive_step_kernel(RecArgs 
 }
 
 // Grid-wide barrier for the persistent ring.  Every workgroup of the grid
-// is co-resident (cooperative launch), arrives once per step on a counter
-// that only grows, and waits until all gridDim.x arrivals of this step are
-// in.  Before arriving, every wave waits until its own stores have reached
-// its XCD's L2 (vmcnt 0); one lane per workgroup then fences at device
-// scope, which writes that L2's dirty lines back to memory, arrives, polls,
-// and fences again after the wait, which drops stale L1 / L2 lines.  A
-// workgroup's HBM stores of one step are therefore seen by every other
+// is co-resident (cooperative launch) and arrives once per barrier.
+//
+// Arrival is two-level: workgroup b counts itself on the counter of group
+// b mod kCtrlGroups (each counter on its own cache line), and the group's
+// last arriver of this barrier adds one arrival to the global counter, so
+// no counter takes more than about gridDim.x / kCtrlGroups atomics per
+// barrier instead of gridDim.x on one address.  Every workgroup then polls
+// the global counter until all groups are in.  Counters only grow, so
+// barrier number `epoch` (from 1) is complete when group g's counter
+// reaches epoch·members(g) and the global counter epoch·groups.
+//
+// Ordering: each wave waits until its own stores have reached its XCD's L2
+// (vmcnt 0) before the workgroup barrier; one lane then issues a release
+// fence at agent scope, which writes that L2's dirty lines back to memory,
+// before arriving.  A group leader fences acquire-release between the
+// group counter and the global counter, which carries its members'
+// releases on; after the wait, an acquire fence drops stale L1 / L2 lines.
+// A workgroup's stores of one step are therefore seen by every other
 // workgroup's loads of the next, across all eight XCDs and their separate
-// L2 caches.  The wait is bounded: after spin_limit polls it raises the
-// abort word, and every workgroup that sees the word stops, so the grid
-// always drains.
-__device__ inline bool grid_barrier(unsigned* ctrl, unsigned target, unsigned spin_limit) {
+// L2 caches.  Release and acquire are separate one-way fences: a full
+// fence on each side would write back and invalidate the caches twice.
+//
+// The wait is bounded: after spin_limit polls a workgroup raises the abort
+// word, and every workgroup that sees the word stops, so the grid always
+// drains.
+__device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spin_limit) {
   __shared__ int s_ok;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned grid = gridDim.x;
+    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
+    const unsigned g = blockIdx.x % unsigned(kCtrlGroups);
+    const unsigned members = (grid - g + kCtrlGroups - 1) / kCtrlGroups;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned before = __hip_atomic_fetch_add(ctrl + kCtrlGroup + g * kCtrlLine, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1u == epoch * members) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     int ok = 1;
     unsigned spins = 0;
-    while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (__hip_atomic_load(ctrl + kCtrlAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u ||
-          ++spins > spin_limit) {
+    while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch * groups) {
+      if (++spins > spin_limit ||
+          ((spins & 63u) == 0u &&
+           __hip_atomic_load(ctrl + kCtrlAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
         __hip_atomic_store(ctrl + kCtrlAbort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     s_ok = ok;
   }
   __syncthreads();
@@ -693,18 +717,15 @@ template <class T, int OP>
 __global__ __launch_bounds__(PersistPolicy::TB) void ring_persistent_kernel(RingArgs a) {
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
-  unsigned arrivals = 0;
+  unsigned epoch = 0;
   for (int step = a.first_step; step < nsteps; ++step) {
-    if (step > a.first_step) {
-      arrivals += gridDim.x;
-      if (!grid_barrier(a.ctrl, arrivals, a.spin_limit)) return;
-    }
+    if (step > a.first_step && !grid_barrier(a.ctrl, ++epoch, a.spin_limit)) return;
     for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, PersistPolicy>(a, step, tile);
   }
 }
 
 __global__ void reset_ctrl_kernel(unsigned* ctrl) {
-  if (threadIdx.x < kCtrlWords) ctrl[threadIdx.x] = 0u;
+  for (int i = threadIdx.x; i < kCtrlWords; i += blockDim.x) ctrl[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------

@@ -136,10 +136,10 @@ def test_workspace_sizes(cs):
     assert ws("allreduce", 8, 1 << 20, "bfloat16", "ring_stepwise") == 2 * 8 * (1 << 17) * 4
     assert ws("allreduce", 2, 1000, "float32", "ring_stepwise") == 0
     assert ws("all_gather", 8, 1000, "float32", "ring_stepwise") == 0
-    assert ws("all_gather", 8, 1000, "float32", "ring_persistent") == 256
+    assert ws("all_gather", 8, 1000, "float32", "ring_persistent") == 1280
     # more than 64 ranks: two pointer tables
     assert ws("allreduce", 256, 1 << 22, "float32", "direct") == 2 * 2048
-    assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == 256 + 4096 + 2 * (1 << 22) * 4
+    assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == 1280 + 4096 + 2 * (1 << 22) * 4
     assert ws("allreduce", 1, 100, "float32", "ring_persistent") == 0
     assert ws("allreduce", 0, 100, "float32", "direct") == ctypes.c_size_t(-1).value
 
