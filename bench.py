@@ -284,18 +284,30 @@ def main():
 
 
 def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
-    """One launch of each kernel the bench times, for hardware counters: the
-    ReduceScatter, the AllGather, and ccl_sim_pad_identity with nothing to
-    pad, a plain copy of N·M elements (reads and writes N·M·s bytes) that
-    calibrates FETCH_SIZE / WRITE_SIZE against a known byte count."""
-    cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", stream=stream)
-    cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", stream=stream)
+    """One call of each kernel the bench times, for hardware counters: the
+    direct ReduceScatter and AllGather, ccl_sim_pad_identity with nothing to
+    pad (a plain copy of N·M elements, reading and writing N·M·s bytes,
+    which calibrates FETCH_SIZE / WRITE_SIZE against a known byte count),
+    then one AllReduce each with the direct, stepwise-ring, persistent-ring
+    and recursive schedules (recursive only for a power-of-two N)."""
+    ws = cs.Workspace.largest([("reduce_scatter", n, m, dtype, "direct"), ("all_gather", n, m, dtype, "direct")])
+    cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", workspace=ws, stream=stream)
+    cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", workspace=ws, stream=stream)
     cs.ccl_sim_pad_identity(send, recv, m, m, "sum", stream=stream)
+    calls = {"rs_direct_kernel": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct"),
+             "ag_direct_kernel": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")}
+    for kernel, schedule in (("ar_direct_kernel", "direct"), ("ring_step_kernel", "ring_stepwise"),
+                             ("ring_persistent_kernel", "ring_persistent"), ("recursive_step_kernel", "recursive")):
+        if schedule == "recursive" and n & (n - 1):
+            continue
+        ws = cs.Workspace("allreduce", n, m, dtype, schedule)
+        cs.ccl_sim_allreduce(send, recv, m, schedule=schedule, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        del ws
+        calls[kernel] = cs.ccl_sim_algorithmic_bytes("allreduce", n, m, dtype, schedule)
     torch.cuda.synchronize()
     es = send[0].element_size()
-    print(json.dumps({"counters_pass": True, "rs_bytes": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype,
-                                                                                      "direct"),
-                      "ag_bytes": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct"),
+    print(json.dumps({"counters_pass": True, "calls": calls,
                       "copy_read_bytes": n * m * es, "copy_write_bytes": n * m * es,
                       "kernel_source_digest": kernel_source_digest()}), flush=True)
 

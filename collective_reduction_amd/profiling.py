@@ -2,17 +2,21 @@
 
     python -m collective_reduction_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
     python -m collective_reduction_amd.profiling traffic <fetch_counter_collection.csv> \
-        <write_counter_collection.csv> <counters_pass_stdout> <workload> <out.json> <command...>
+        <write_counter_collection.csv> <counters_pass_stdout> <workload> <out.json> <out.md>
 
 ``stats`` keeps the per-kernel call count and durations of a
 ``--kernel-trace --stats`` run.  ``traffic`` reads two ``--pmc`` runs of
 ``bench.py --counters-pass`` (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) and scales each counter by what it reads for the plain copy in
 the same pass (``ccl_sim_pad_identity`` with nothing to pad, which reads
-and writes a known N·M·s bytes), giving HBM bytes per launch of the
-ReduceScatter and AllGather kernels.  The record carries the digest of the
-kernel sources the counters were taken on; bench.py reports the traffic
-only while that digest still matches.
+and writes a known N·M·s bytes).  For each call of the pass it sums the
+counters over the call's dispatches of its kernel (one for the direct
+kernels and the persistent ring, 2(N-1) for the stepwise ring, 2·log2 N for
+the recursive schedule) and sets the HBM bytes beside the call's
+algorithmic bytes.  It writes ``profiles/traffic.json`` and a Markdown
+table of the same figures.  The record carries the digest of the kernel
+sources the counters were taken on; bench.py reports the traffic only
+while that digest still matches.
 """
 
 import csv
@@ -23,7 +27,8 @@ import sys
 
 def _short(name):
     for key in ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
-                "ring_persistent_kernel", "pad_kernel", "reset_ctrl_kernel", "store_table_kernel"):
+                "ring_persistent_kernel", "recursive_step_kernel", "pad_kernel", "reset_ctrl_kernel",
+                "store_table_kernel"):
         if key in name:
             return key
     return name
@@ -34,7 +39,7 @@ def stats(stats_csv, out_md, command):
     lines = [
         "# rocprofv3 kernel statistics",
         "",
-        "Command (from the repository root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):",
+        "Command (run from `/tmp` with `TMPDIR=/tmp`; `<repo>` is the repository root):",
         "",
         "```",
         command,
@@ -60,7 +65,7 @@ def _counter(path):
     return vals
 
 
-def traffic(fetch_csv, write_csv, pass_out, workload, out_json, command):
+def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command):
     info = None
     for line in open(pass_out):
         line = line.strip()
@@ -72,19 +77,23 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, command):
     fscale = info["copy_read_bytes"] / (fetch["pad_kernel"][0] * 1024)
     wscale = info["copy_write_bytes"] / (write["pad_kernel"][0] * 1024)
     rec = {}
-    if os.path.exists(out_json):
-        rec = json.load(open(out_json))
-    for kernel, algo in (("rs_direct_kernel", info["rs_bytes"]), ("ag_direct_kernel", info["ag_bytes"])):
-        rd = fetch[kernel][0] * 1024 * fscale
-        wr = write[kernel][0] * 1024 * wscale
+    for kernel, algo in info["calls"].items():
+        if len(fetch[kernel]) != len(write[kernel]):
+            raise SystemExit(f"{kernel}: {len(fetch[kernel])} FETCH_SIZE and {len(write[kernel])} WRITE_SIZE records")
+        k = len(fetch[kernel])
+        rd = sum(fetch[kernel]) * 1024 * fscale
+        wr = sum(write[kernel]) * 1024 * wscale
         rec[f"{kernel}:{workload}"] = {
-            "traffic_bytes": rd + wr,
-            "read_bytes": rd,
-            "write_bytes": wr,
-            "algorithmic_bytes": algo,
+            "dispatches": k,
+            "traffic_bytes": (rd + wr) / k,
+            "read_bytes": rd / k,
+            "write_bytes": wr / k,
+            "algorithmic_bytes": algo / k,
+            "call_traffic_bytes": rd + wr,
+            "call_algorithmic_bytes": algo,
             "traffic_over_algorithmic": (rd + wr) / algo,
-            "fetch_size_kib": fetch[kernel][0],
-            "write_size_kib": write[kernel][0],
+            "fetch_size_kib": sum(fetch[kernel]),
+            "write_size_kib": sum(write[kernel]),
             "fetch_scale": fscale,
             "write_scale": wscale,
             "calibration": "ccl_sim_pad_identity with count == padded_count (plain copy of N*M elements)",
@@ -94,7 +103,47 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, command):
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
+    _traffic_md(rec, workload, info, fscale, wscale, out_md, command)
     return rec
+
+
+def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
+    what = {"rs_direct_kernel": "ReduceScatter, direct", "ag_direct_kernel": "AllGather, direct",
+            "ar_direct_kernel": "AllReduce, direct (one kernel)",
+            "ring_step_kernel": "AllReduce, stepwise ring (all steps)",
+            "ring_persistent_kernel": "AllReduce, persistent ring (one launch)",
+            "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)"}
+    lines = [
+        f"# HBM traffic of the library's kernels (rocprofv3 counters), {workload}",
+        "",
+        "Commands (from `/tmp` with `TMPDIR=/tmp`; `<repo>` is the repository root):",
+        "",
+        "```",
+        f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py --counters-pass",
+        f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py --counters-pass",
+        command,
+        "```",
+        "",
+        f"Calibration: the same pass runs `ccl_sim_pad_identity` with nothing to pad, a plain copy that reads and "
+        f"writes exactly {info['copy_read_bytes']:,} bytes. FETCH_SIZE reports {1 / fscale:.4f} of the bytes read "
+        f"and WRITE_SIZE {1 / wscale:.6f} of the bytes written; every kernel's counters are multiplied by those "
+        f"factors. Figures are per call, summed over the call's dispatches.",
+        "",
+        "| call | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B | traffic B "
+        "| algorithmic B | traffic / algorithmic |",
+        "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|",
+    ]
+    for key, r in rec.items():
+        kernel = key.split(":")[0]
+        lines.append(
+            f"| {what.get(kernel, kernel)} | `{kernel}` | {r['dispatches']} | {r['fetch_size_kib']:.1f} | "
+            f"{r['write_size_kib']:.1f} | {r['read_bytes'] * r['dispatches']:.4e} | "
+            f"{r['write_bytes'] * r['dispatches']:.4e} | {r['call_traffic_bytes']:.4e} | "
+            f"{r['call_algorithmic_bytes']:.4e} | {r['traffic_over_algorithmic']:.5f} |")
+    lines += ["", f"Kernel source digest the counters were taken on: `{info['kernel_source_digest']}` (bench.py "
+              "reports `traffic` only while the sources still hash to it)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":
@@ -102,6 +151,7 @@ if __name__ == "__main__":
     if mode == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif mode == "traffic":
-        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], " ".join(sys.argv[7:]))
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
+                "python -m collective_reduction_amd.profiling " + " ".join(sys.argv[1:]))
     else:
         raise SystemExit(__doc__)
