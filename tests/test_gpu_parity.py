@@ -151,6 +151,38 @@ def test_allreduce_tiny_and_empty(cs, schedule):
     cs.ccl_sim_allreduce(z, z, 0, schedule=schedule, dtype="float32")
 
 
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+@pytest.mark.parametrize("op", ("max", "min"))
+@pytest.mark.parametrize("dtype", ("float32", "bfloat16"))
+def test_signed_zero_ties_follow_the_combining_order(cs, dtype, op, schedule):
+    """+0 and -0 compare equal, and a tie keeps the left operand (the running
+    partial).  With inputs that are random signed zeros, the sign of each
+    result names the operand that survived, so the GPU must reproduce the
+    schedule's combining order and its tie rule exactly: ascending ranks for
+    the direct schedule, chunk owner first for the ring, lower rank of each
+    pair for the recursive butterfly."""
+    n, q = 8, 37
+    rng = np.random.default_rng([len(dtype), len(op), U.SCHEDULES.index(schedule)])
+    neg = [rng.random(n * q) < 0.5 for _ in range(n)]
+    if dtype == "float32":
+        xs = [np.where(k, np.float32(-0.0), np.float32(0.0)).astype(np.float32) for k in neg]
+    else:
+        xs = [np.where(k, 0x8000, 0x0000).astype(np.uint16) for k in neg]
+    for m in (n * q, n * q - 5):
+        ins = [x[:m] for x in xs]
+        got = U.run_ar(cs, ins, op, dtype, schedule)
+        assert_all_same(got, oracle_ar(ins, op, dtype, schedule)[0], f"AR m={m}")
+    got = U.run_rs(cs, xs, q, op, dtype, schedule)
+    want = oracle_rs(xs, op, dtype, q, schedule)
+    for r in range(n):
+        assert U.same_bits(got[r], want[r]), f"RS rank {r}"
+    # the ring's order really differs: direct (and the recursive butterfly,
+    # lower rank on the left at every level) keep rank 0's sign everywhere
+    if schedule.startswith("ring"):
+        direct = C.direct_allreduce(xs, op, dtype)[0]
+        assert not U.same_bits(oracle_ar(xs, op, dtype, schedule)[0], direct)
+
+
 def test_recursive_needs_a_power_of_two(cs):
     xs = U.random_inputs(6, 60, "float32", seed=1)
     with pytest.raises(cs.CclSimError, match="power-of-two"):

@@ -15,7 +15,9 @@ import numpy as np
 import pytest
 
 import test_oracle_pins as P
+import test_oracle_recursive as Q
 from oracle import collectives as C
+from oracle import recursive as H
 from oracle import reduction as R
 from oracle import ring as G
 
@@ -46,6 +48,12 @@ PINS = [
     lambda: P.test_bf16_rounding_cases(),
     lambda: P.test_gradient_like_256_ranks_tolerance(),
     lambda: P.test_avg_is_the_sum_divided_once(),
+    lambda: Q.test_pair_table_and_volumes(_golden),
+    lambda: Q.test_onehot_partials_cover_the_pair_groups(),
+    lambda: Q.test_brute_force_integers(),
+    lambda: Q.test_butterfly_order_float32(),
+    lambda: Q.test_max_ties_keep_the_lower_ranks_partial(),
+    lambda: Q.test_doubling_all_gather_and_trim(),
 ]
 
 
@@ -114,6 +122,53 @@ def _finalize_by_n_minus_1(op, acc, nranks):
     return _ORIG_FINALIZE(op, acc, nranks - 1 if nranks > 1 else 1)
 
 
+def _halving_pairs_doubling_distance(nranks):
+    k = nranks.bit_length() - 1
+    return [[(i, i ^ (1 << (j - 1))) for i in range(nranks) if i < (i ^ (1 << (j - 1)))] for j in range(1, k + 1)]
+
+
+def _kept_range_swapped(nranks, q, step, rank):
+    lo, length = 0, nranks * q
+    for j in range(1, step + 1):
+        length //= 2
+        if not rank & (nranks >> j):
+            lo += length
+    return lo, lo + length
+
+
+def _rh_phase_upper_left(bufs, op, q, record):
+    n = len(bufs)
+    states = []
+    for j in range(1, n.bit_length()):
+        d = n >> j
+        new = [b.copy() for b in bufs]
+        for i in range(n):
+            p = i ^ d
+            lo, hi = H.kept_range(n, q, j, i)
+            low, up = (i, p) if i < p else (p, i)
+            new[i][lo:hi] = R.combine(op, bufs[up][lo:hi], bufs[low][lo:hi])
+        bufs[:] = new
+        if record:
+            states.append([b.copy() for b in bufs])
+    return states
+
+
+def _rd_phase_own_block(bufs, q, record):
+    n = len(bufs)
+    states = []
+    for t in range(n.bit_length() - 1):
+        new = [b.copy() for b in bufs]
+        for i in range(n):
+            p = i ^ (1 << t)
+            lo = ((i >> t) << t) * q
+            hi = (((i >> t) + 1) << t) * q
+            new[i][lo:hi] = bufs[p][lo:hi]
+        bufs[:] = new
+        if record:
+            states.append([b.copy() for b in bufs])
+    return states
+
+
 _ORIG_FOLD = C.fold
 _ORIG_GATHER = C.all_gather
 _ORIG_COMBINE = R.combine
@@ -132,6 +187,10 @@ MUTANTS = {
     "ring owner is the rank itself": (G, "ring_owner", _owner_same_rank),
     "integer AVG rounds toward minus infinity": (R, "finalize", _finalize_floor),
     "AVG divides by N-1": (R, "finalize", _finalize_by_n_minus_1),
+    "halving pairs at the doubling distances": (H, "halving_pairs", _halving_pairs_doubling_distance),
+    "halving keeps the other half": (H, "kept_range", _kept_range_swapped),
+    "halving combines upper rank on the left": (H, "_rh_phase", _rh_phase_upper_left),
+    "doubling copies the receiver's own block": (H, "_rd_phase", _rd_phase_own_block),
 }
 
 

@@ -98,6 +98,20 @@ def test_butterfly_order_float32():
     assert R.normalized_sum_error(got, xs, "float32") <= (n - 1) * 2.0 ** -24
 
 
+def test_max_ties_keep_the_lower_ranks_partial():
+    """Operand order inside each pair: under MAX a tie keeps the left operand
+    (max(a, b) = b > a ? b : a), and +0 and -0 tie.  With every input a
+    signed zero, the butterfly keeps the lower rank's partial at every
+    step, so every result carries the sign of rank 0's input."""
+    n, q = 8, 16
+    rng = np.random.default_rng(7)
+    xs = [np.where(rng.random(n * q) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+          for _ in range(n)]
+    got = np.concatenate(H.reduce_scatter(xs, "max", "float32", q))
+    assert np.array_equal(np.signbit(got), np.signbit(xs[0]))
+    assert not np.array_equal(np.signbit(xs[0]), np.signbit(xs[n - 1]))
+
+
 def test_doubling_all_gather_and_trim():
     n, q = 8, 7
     rng = np.random.default_rng(1)
