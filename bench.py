@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -48,10 +49,15 @@ def parse():
 
 
 def kernel_source_digest():
+    """Digest of the device code's source: comments and whitespace are
+    dropped first, so a comment edit does not count as a kernel change."""
     h = hashlib.sha256()
     for name in ("kernels.hip", "device.hpp", "internal.hpp"):
-        with open(os.path.join(HERE, "collective_reduction_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, "collective_reduction_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,12 +1,14 @@
 // HIP kernels for gfx950: fused N-way reduce (ReduceScatter), broadcast-copy
 // (AllGather), fused AllReduce, ring steps (one launch per step, or one
-// persistent cooperative kernel with a grid barrier), identity padding.
+// persistent cooperative kernel with a grid barrier), recursive halving and
+// doubling steps, identity padding.
 //
 // Pages cited:
-//   [DECOMP] "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
-//   [RING]   "Ring AllReduce 核心流程：梯度是怎么聚合的"
-//   [PRIMS]  "通信与互联（01）：集合通信原语与代价模型——α-β 模型与 ring all-reduce"
-//   [WHY-EQ] "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
+//   [DECOMP]  "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
+//   [RING]    "Ring AllReduce 核心流程：梯度是怎么聚合的"
+//   [PRIMS]   "通信与互联（01）：集合通信原语与代价模型——α-β 模型与 ring all-reduce"
+//   [WHY-EQ]  "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
+//   [RS-PAGE] "ReduceScatter" (集合通信)
 //
 // Work decomposition.  Every kernel is a grid-stride loop over tiles of
 // TB·V·U elements (V = 16 / sizeof(element): one 128-bit access per lane

@@ -39,10 +39,11 @@
  * Workspace. Device scratch of at least ccl_sim_workspace_size(...) bytes,
  *            256-byte aligned, owned by the caller.  It carries the device
  *            copy of the pointer tables when nranks > 64, the partial sums
- *            the ring schedules pass between ranks, and the grid-barrier
- *            counter of the persistent ring.  Calls that share a workspace
- *            must be ordered on one stream.  NULL is allowed when the
- *            required size is 0.
+ *            the ring schedules pass between ranks, the per-rank halves of
+ *            the recursive halving schedule, and the barrier block (arrival
+ *            counters and an abort word) of the persistent ring.  Calls
+ *            that share a workspace must be ordered on one stream.  NULL is
+ *            allowed when the required size is 0.
  * Errors.    Every argument is validated before any HIP call; on any error
  *            nothing is enqueued and the output buffers are untouched (as the
  *            capacity check of [DECOMP] §Contract 实验四 rejects a
@@ -211,10 +212,15 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
  * AllGather, count for AllReduce.  q = ceil(M / N) is the shard length.
  *
  * Workspace bytes one call needs (0 when none, SIZE_MAX for invalid
- * arguments): the pointer tables when nranks > 64, the ring's double-
- * buffered partials 2·N·q·a (a = accumulator size: 4 for bf16, else the
- * element size) for ring ReduceScatter and ring AllReduce with N >= 3, and
- * a barrier block for the persistent ring.
+ * arguments), each part rounded up to 256 bytes:
+ *   - a barrier block of 1152 bytes for the persistent ring;
+ *   - two pointer tables of 8·N bytes each when nranks > 64;
+ *   - the ring's double-buffered partials 2·N·q·a (a = accumulator size: 4
+ *     for bf16, else the element size) for ring ReduceScatter and ring
+ *     AllReduce with N >= 3;
+ *   - the recursive schedule's per-rank halves N·(N/2)·q·a for its
+ *     ReduceScatter and AllReduce with N >= 4.
+ * AllGather needs no partials under any schedule.
  */
 size_t ccl_sim_workspace_size(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_dtype_t dtype,
                               ccl_sim_schedule_t schedule);
