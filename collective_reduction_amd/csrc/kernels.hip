@@ -80,6 +80,9 @@ struct Policy {
 #ifndef CCL_SIM_RING_POLICY
 #define CCL_SIM_RING_POLICY 256, 1, true, kStoreWriteThrough
 #endif
+#ifndef CCL_SIM_RING_SMALL_POLICY
+#define CCL_SIM_RING_SMALL_POLICY 256, 2, true, kStoreWriteThrough
+#endif
 #ifndef CCL_SIM_PERSIST_POLICY
 #define CCL_SIM_PERSIST_POLICY 256, 4, true, kStoreWriteThrough
 #endif
@@ -90,6 +93,7 @@ using RsPolicy = Policy<CCL_SIM_RS_POLICY>;
 using AgPolicy = Policy<CCL_SIM_AG_POLICY>;
 using ArPolicy = Policy<CCL_SIM_AR_POLICY>;
 using RingPolicy = Policy<CCL_SIM_RING_POLICY>;
+using RingSmallPolicy = Policy<CCL_SIM_RING_SMALL_POLICY>;
 using PersistPolicy = Policy<CCL_SIM_PERSIST_POLICY>;
 using PadPolicy = Policy<CCL_SIM_PAD_POLICY>;
 
@@ -574,9 +578,9 @@ __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
   }
 }
 
-template <class T, int OP>
-__global__ __launch_bounds__(RingPolicy::TB) void ring_step_kernel(RingArgs a) {
-  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, RingPolicy>(a, a.step, tile);
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ring_step_kernel(RingArgs a) {
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P>(a, a.step, tile);
 }
 
 // ---------------------------------------------------------------------------
@@ -615,10 +619,9 @@ struct RecArgs {
   void* scratch;
 };
 
-template <class T, int OP, bool FULL>
+template <class T, int OP, class P, bool FULL>
 __device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint64_t base, uint64_t cnt) {
   using A = typename T::A;
-  using P = RingPolicy;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const int n = a.nranks;
@@ -676,9 +679,9 @@ __device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint6
   }
 }
 
-template <class T, int OP>
-__global__ __launch_bounds__(RingPolicy::TB) void recursive_step_kernel(RecArgs a) {
-  constexpr uint64_t kTile = tile_of<RingPolicy>(vec_elems<T>());
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void recursive_step_kernel(RecArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int i = rank_of_tile(tile, a.tiles_per_rank);
     const uint64_t seg = tile - uint64_t(i) * a.tiles_per_rank;
@@ -699,15 +702,15 @@ __global__ __launch_bounds__(RingPolicy::TB) void recursive_step_kernel(RecArgs 
     const bool full = (seg + 1) * kTile <= cnt;
     if (a.phase == 0) {
       if (full)
-        halving_tile<T, OP, true>(a, i, seg, base, cnt);
+        halving_tile<T, OP, P, true>(a, i, seg, base, cnt);
       else
-        halving_tile<T, OP, false>(a, i, seg, base, cnt);
+        halving_tile<T, OP, P, false>(a, i, seg, base, cnt);
     } else {
       typename T::S* dst = out_ptr<T>(a.recv, i) + base;
       if (full)
-        copy_tile<T, RingPolicy, true>(src, dst, seg, cnt);
+        copy_tile<T, P, true>(src, dst, seg, cnt);
       else
-        copy_tile<T, RingPolicy, false>(src, dst, seg, cnt);
+        copy_tile<T, P, false>(src, dst, seg, cnt);
     }
   }
 }
@@ -968,22 +971,41 @@ hipError_t run_direct(const Call& c) {
   });
 }
 
+// Launch shape of the step kernels by step size.  A step that moves few
+// elements is over before a one-vector-per-lane grid has ramped up, and two
+// vectors per lane (half the workgroups) measured faster there; large steps
+// are faster with one.  The crossovers, measured on float32 with N = 8 to
+// 256: a ring step (N chunks of q) up to 2^26 elements, a recursive
+// halving or doubling step up to 2^24.
+#ifndef CCL_SIM_RING_SMALL_STEP
+#define CCL_SIM_RING_SMALL_STEP (uint64_t(1) << 26)
+#endif
+#ifndef CCL_SIM_RECURSIVE_SMALL_STEP
+#define CCL_SIM_RECURSIVE_SMALL_STEP (uint64_t(1) << 24)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_ring_steps(const Call& c) {
+  RingArgs a = make_ring_args(c, tile_elems<T, P>());
+  const unsigned grid = grid_for(a.ntiles, c.num_cus);
+  const int n = c.nranks;
+  const int nsteps = (c.coll == kAllReduce) ? 2 * (n - 1) : (c.coll == kReduceScatter ? n - 1 : n);
+  const int first = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  for (int step = first; step < nsteps; ++step) {
+    a.step = step;
+    hipLaunchKernelGGL((ring_step_kernel<T, OP, P>), dim3(grid), dim3(P::TB), 0, c.stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t run_ring_stepwise(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    RingArgs a = make_ring_args(c, tile_elems<T, RingPolicy>());
-    const unsigned grid = grid_for(a.ntiles, c.num_cus);
-    const int n = c.nranks;
-    const int nsteps = (c.coll == kAllReduce) ? 2 * (n - 1) : (c.coll == kReduceScatter ? n - 1 : n);
-    const int first = (c.coll == kAllGather && c.in_place) ? 1 : 0;
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    const bool small = uint64_t(c.nranks) * c.q <= CCL_SIM_RING_SMALL_STEP;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
-      for (int step = first; step < nsteps; ++step) {
-        a.step = step;
-        hipLaunchKernelGGL((ring_step_kernel<U, OP>), dim3(grid), dim3(RingPolicy::TB), 0, c.stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      return hipSuccess;
+      return small ? launch_ring_steps<U, OP, RingSmallPolicy>(c) : launch_ring_steps<U, OP, RingPolicy>(c);
     });
   });
 }
@@ -1041,11 +1063,25 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan*
   });
 }
 
+template <class T, int OP, class P>
+hipError_t launch_recursive_step(const Call& c, RecArgs& a, int phase, int step, int k, uint64_t len) {
+  const uint64_t tile = tile_elems<T, P>();
+  a.phase = phase;
+  a.step = step;
+  a.last = (phase == 0 && step == k) ? 1 : 0;
+  a.len = len;
+  a.tiles_per_rank = ceil_div(len, tile);
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_rank;
+  if (a.ntiles == 0) return hipSuccess;
+  const unsigned grid = grid_for(a.ntiles, c.num_cus);
+  hipLaunchKernelGGL((recursive_step_kernel<T, OP, P>), dim3(grid), dim3(P::TB), 0, c.stream, a);
+  return hipGetLastError();
+}
+
 hipError_t run_recursive(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
-      const uint64_t tile = tile_elems<U, RingPolicy>();
       const int n = c.nranks;
       int k = 0;
       while ((1 << k) < n) ++k;
@@ -1058,16 +1094,9 @@ hipError_t run_recursive(const Call& c) {
       a.limit = c.limit;
       a.scratch = c.partial;
       auto launch = [&](int phase, int step, uint64_t len) -> hipError_t {
-        a.phase = phase;
-        a.step = step;
-        a.last = (phase == 0 && step == k) ? 1 : 0;
-        a.len = len;
-        a.tiles_per_rank = ceil_div(len, tile);
-        a.ntiles = uint64_t(n) * a.tiles_per_rank;
-        if (a.ntiles == 0) return hipSuccess;
-        const unsigned grid = grid_for(a.ntiles, c.num_cus);
-        hipLaunchKernelGGL((recursive_step_kernel<U, OP>), dim3(grid), dim3(RingPolicy::TB), 0, c.stream, a);
-        return hipGetLastError();
+        if (uint64_t(n) * len <= CCL_SIM_RECURSIVE_SMALL_STEP)
+          return launch_recursive_step<U, OP, RingSmallPolicy>(c, a, phase, step, k, len);
+        return launch_recursive_step<U, OP, RingPolicy>(c, a, phase, step, k, len);
       };
       hipError_t e = hipSuccess;
       if (c.coll != kAllGather)
