@@ -323,10 +323,11 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
       return fail(CCL_SIM_UNSUPPORTED, "no co-resident grid for the persistent ring kernel on this device");
     if (c.log_plan)
       std::fprintf(stderr,
-                   "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu "
+                   "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu lanes=%d "
                    "tiles/step=%llu\n",
                    coll, nranks, static_cast<unsigned long long>(q), c.num_cus, plan.occupancy_per_cu, plan.per_cu,
-                   static_cast<unsigned long long>(plan.grid), static_cast<unsigned long long>(plan.tiles_per_step));
+                   static_cast<unsigned long long>(plan.grid), plan.lanes,
+                   static_cast<unsigned long long>(plan.tiles_per_step));
     if (e == hipSuccess && c.log_plan) {
       // Debug check of the barrier's watchdog: wait for the kernel and read
       // the abort word it raises when a barrier runs into the poll limit.

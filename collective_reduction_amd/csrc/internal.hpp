@@ -38,9 +38,9 @@ struct PersistentPlan {
   int per_cu = 0;
   uint64_t grid = 0;
   uint64_t tiles_per_step = 0;
+  int lanes = 0;  // threads per workgroup
 };
 
-// Control block layout (unsigned words) at the start of the workspace.
 // Control block of the persistent ring (unsigned words): line 0 holds the
 // global arrival counter and the abort word, line 1 + g the arrival counter
 // of barrier group g; a line is 128 bytes.

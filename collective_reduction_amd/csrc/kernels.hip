@@ -86,6 +86,9 @@ struct Policy {
 #ifndef CCL_SIM_PERSIST_POLICY
 #define CCL_SIM_PERSIST_POLICY 256, 4, true, kStoreWriteThrough
 #endif
+#ifndef CCL_SIM_PERSIST_SMALL_POLICY
+#define CCL_SIM_PERSIST_SMALL_POLICY 1024, 4, true, kStoreWriteThrough
+#endif
 #ifndef CCL_SIM_PAD_POLICY
 #define CCL_SIM_PAD_POLICY 256, 4, false, kStorePlain
 #endif
@@ -95,6 +98,7 @@ using ArPolicy = Policy<CCL_SIM_AR_POLICY>;
 using RingPolicy = Policy<CCL_SIM_RING_POLICY>;
 using RingSmallPolicy = Policy<CCL_SIM_RING_SMALL_POLICY>;
 using PersistPolicy = Policy<CCL_SIM_PERSIST_POLICY>;
+using PersistSmallPolicy = Policy<CCL_SIM_PERSIST_SMALL_POLICY>;
 using PadPolicy = Policy<CCL_SIM_PAD_POLICY>;
 
 template <class P>
@@ -776,14 +780,14 @@ __device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spi
   return s_ok != 0;
 }
 
-template <class T, int OP>
-__global__ __launch_bounds__(PersistPolicy::TB) void ring_persistent_kernel(RingArgs a) {
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
   unsigned epoch = 0;
   for (int step = a.first_step; step < nsteps; ++step) {
     if (step > a.first_step && !grid_barrier(a.ctrl, ++epoch, a.spin_limit)) return;
-    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, PersistPolicy>(a, step, tile);
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P>(a, step, tile);
   }
 }
 
@@ -1014,51 +1018,68 @@ hipError_t run_ring_stepwise(const Call& c) {
 #define CCL_SIM_PERSISTENT_PER_CU 1
 #endif
 
+// The persistent grid holds one workgroup per CU (see below), so its lanes
+// alone must keep enough loads in flight.  For steps of up to 2^26
+// elements a 1024-lane workgroup (a step of N = 256 chunks of 2^14 float32
+// is then one tile per workgroup) measured 9-17 % faster than 256 lanes;
+// for larger steps 256 lanes were faster.
+#ifndef CCL_SIM_PERSIST_SMALL_STEP
+#define CCL_SIM_PERSIST_SMALL_STEP (uint64_t(1) << 26)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
+  RingArgs a = make_ring_args(c, tile_elems<T, P>());
+  a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  if (c.spin_limit) a.spin_limit = c.spin_limit;
+  auto kernel = ring_persistent_kernel<T, OP, P>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, P::TB, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu <= 0 || c.num_cus <= 0) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  // Workgroups per CU: at most what the occupancy calculation allows, and
+  // by default only CCL_SIM_PERSISTENT_PER_CU of them.  A grid at the full
+  // occupancy figure was found not to be co-resident on MI355X (its first
+  // barrier ran into the poll limit); of the grids that are, one workgroup
+  // per CU measured fastest, at every step size: the barrier's cost grows
+  // with the number of workgroups that arrive.
+  const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
+  const int use = want < per_cu ? want : per_cu;
+  uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
+  if (grid > a.ntiles) grid = a.ntiles;
+  if (grid == 0) grid = 1;
+  if (plan) {
+    plan->occupancy_per_cu = per_cu;
+    plan->per_cu = use;
+    plan->grid = grid;
+    plan->tiles_per_step = a.ntiles;
+    plan->lanes = P::TB;
+  }
+  hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void* args[] = {&a};
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)), dim3(P::TB),
+                                 args, 0, c.stream);
+  if (e == hipErrorCooperativeLaunchTooLarge) {
+    (void)hipGetLastError();
+    *unsupported = true;
+    return hipSuccess;
+  }
+  return e;
+}
+
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
   *unsupported = false;
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    RingArgs a = make_ring_args(c, tile_elems<T, PersistPolicy>());
-    a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
-    if (c.spin_limit) a.spin_limit = c.spin_limit;
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    const bool small = uint64_t(c.nranks) * c.q <= CCL_SIM_PERSIST_SMALL_STEP;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
-      auto kernel = ring_persistent_kernel<U, OP>;
-      int per_cu = 0;
-      hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, PersistPolicy::TB, 0);
-      if (e != hipSuccess) return e;
-      if (per_cu <= 0 || c.num_cus <= 0) {
-        *unsupported = true;
-        return hipSuccess;
-      }
-      // Workgroups per CU: at most what the occupancy calculation allows,
-      // and by default only CCL_SIM_PERSISTENT_PER_CU of them.  A grid at
-      // the full occupancy figure was found not to be co-resident on MI355X
-      // (its first barrier ran into the poll limit); of the grids that are,
-      // one workgroup per CU measured fastest, since every barrier costs
-      // each workgroup an L2 write-back.
-      const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
-      const int use = want < per_cu ? want : per_cu;
-      uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
-      if (grid > a.ntiles) grid = a.ntiles;
-      if (grid == 0) grid = 1;
-      if (plan) {
-        plan->occupancy_per_cu = per_cu;
-        plan->per_cu = use;
-        plan->grid = grid;
-        plan->tiles_per_step = a.ntiles;
-      }
-      hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      void* args[] = {&a};
-      e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)),
-                                     dim3(PersistPolicy::TB), args, 0, c.stream);
-      if (e == hipErrorCooperativeLaunchTooLarge) {
-        (void)hipGetLastError();
-        *unsupported = true;
-        return hipSuccess;
-      }
-      return e;
+      return small ? launch_persistent<U, OP, PersistSmallPolicy>(c, unsupported, plan)
+                   : launch_persistent<U, OP, PersistPolicy>(c, unsupported, plan);
     });
   });
 }
