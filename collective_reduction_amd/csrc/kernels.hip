@@ -77,6 +77,9 @@ struct Policy {
 #ifndef CCL_SIM_AR_POLICY
 #define CCL_SIM_AR_POLICY 256, 1, true, kStoreWriteThrough
 #endif
+#ifndef CCL_SIM_DIRECT_SMALL_POLICY
+#define CCL_SIM_DIRECT_SMALL_POLICY 256, 2, true, kStoreWriteThrough
+#endif
 #ifndef CCL_SIM_RING_POLICY
 #define CCL_SIM_RING_POLICY 256, 1, true, kStoreWriteThrough
 #endif
@@ -95,6 +98,7 @@ struct Policy {
 using RsPolicy = Policy<CCL_SIM_RS_POLICY>;
 using AgPolicy = Policy<CCL_SIM_AG_POLICY>;
 using ArPolicy = Policy<CCL_SIM_AR_POLICY>;
+using DirectSmallPolicy = Policy<CCL_SIM_DIRECT_SMALL_POLICY>;
 using RingPolicy = Policy<CCL_SIM_RING_POLICY>;
 using RingSmallPolicy = Policy<CCL_SIM_RING_SMALL_POLICY>;
 using PersistPolicy = Policy<CCL_SIM_PERSIST_POLICY>;
@@ -298,9 +302,8 @@ struct ShardArgs {
 // ReduceScatter: recv[r][j] = ⊕_s send[s][r·q + j] ([DECOMP] §数学证明;
 // [RS-PAGE] equation rs-semantic-output).  One pass over the N inputs, one
 // write of the shards: (N+1)·M elements of HBM traffic.
-template <class T, int OP, bool FULL>
+template <class T, int OP, class P, bool FULL>
 __device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
-  using P = RsPolicy;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const L ln(seg, a.q);
@@ -312,16 +315,16 @@ __device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
     if (ln.on(u)) ln.store(out, u, finish_vec<T, OP, typename L::SV>(acc[u], a.nranks));
 }
 
-template <class T, int OP>
-__global__ __launch_bounds__(RsPolicy::TB) void rs_direct_kernel(ShardArgs a) {
-  constexpr uint64_t kTile = tile_of<RsPolicy>(vec_elems<T>());
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void rs_direct_kernel(ShardArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int r = rank_of_tile(tile, a.tiles_per_shard);
     const uint64_t seg = tile - uint64_t(r) * a.tiles_per_shard;
     if ((seg + 1) * kTile <= a.q)
-      rs_tile<T, OP, true>(a, r, seg);
+      rs_tile<T, OP, P, true>(a, r, seg);
     else
-      rs_tile<T, OP, false>(a, r, seg);
+      rs_tile<T, OP, P, false>(a, r, seg);
   }
 }
 
@@ -387,9 +390,8 @@ struct FlatArgs {
 
 // Direct AllReduce in one kernel: y^(r)_i = ⊕_s x^(s)_i stored to all N
 // outputs ([DECOMP] §数学证明 Direct AllReduce): 2N·M elements of traffic.
-template <class T, int OP, bool FULL>
+template <class T, int OP, class P, bool FULL>
 __device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
-  using P = ArPolicy;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const L ln(tile, a.count);
@@ -407,14 +409,14 @@ __device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
   }
 }
 
-template <class T, int OP>
-__global__ __launch_bounds__(ArPolicy::TB) void ar_direct_kernel(FlatArgs a) {
-  constexpr uint64_t kTile = tile_of<ArPolicy>(vec_elems<T>());
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ar_direct_kernel(FlatArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     if ((tile + 1) * kTile <= a.count)
-      ar_tile<T, OP, true>(a, tile);
+      ar_tile<T, OP, P, true>(a, tile);
     else
-      ar_tile<T, OP, false>(a, tile);
+      ar_tile<T, OP, P, false>(a, tile);
   }
 }
 
@@ -939,39 +941,63 @@ size_t elem_size(int dtype) {
 
 size_t accum_size(int dtype) { return dtype == kBFloat16 ? 4 : elem_size(dtype); }
 
+// The fused reductions (ReduceScatter and AllReduce) take two vectors per
+// lane when a call produces at most 2^24 elements per output set (M for
+// the AllReduce, N·q for the ReduceScatter): each lane then keeps twice as
+// many rank loads in flight, which measured 7-9 % faster there (N = 8 at
+// M = 2^24, N = 256 at M = 2^22) and 3 % slower at M = 2^28.  The
+// AllGather keeps one vector per lane at every size.
+#ifndef CCL_SIM_DIRECT_SMALL_CALL
+#define CCL_SIM_DIRECT_SMALL_CALL (uint64_t(1) << 24)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_ar_direct(const Call& c) {
+  FlatArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.count = c.limit;
+  a.ntiles = ceil_div(c.limit, tile_elems<T, P>());
+  hipLaunchKernelGGL((ar_direct_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0, c.stream, a);
+  return hipGetLastError();
+}
+
+template <class P, class T>
+ShardArgs shard_args(const Call& c) {
+  ShardArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.q = c.q;
+  a.tiles_per_shard = ceil_div(c.q, tile_elems<T, P>());
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_shard;
+  a.limit = c.limit;
+  return a;
+}
+
+template <class T, int OP, class P>
+hipError_t launch_rs_direct(const Call& c) {
+  const ShardArgs a = shard_args<P, T>(c);
+  hipLaunchKernelGGL((rs_direct_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0, c.stream, a);
+  return hipGetLastError();
+}
+
 hipError_t run_direct(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
-    if (c.coll == kAllReduce) {
-      FlatArgs a{};
-      a.send = c.send;
-      a.recv = c.recv;
-      a.nranks = c.nranks;
-      a.count = c.limit;
-      a.ntiles = ceil_div(c.limit, tile_elems<T, ArPolicy>());
-      const unsigned grid = grid_for(a.ntiles, c.num_cus);
-      return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
-        hipLaunchKernelGGL((ar_direct_kernel<U, OP>), dim3(grid), dim3(ArPolicy::TB), 0, c.stream, a);
-        return hipGetLastError();
-      });
+    if (c.coll == kAllGather) {
+      const ShardArgs a = shard_args<AgPolicy, T>(c);
+      hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(AgPolicy::TB), 0, c.stream,
+                         a);
+      return hipGetLastError();
     }
-    ShardArgs a{};
-    a.send = c.send;
-    a.recv = c.recv;
-    a.nranks = c.nranks;
-    a.q = c.q;
-    a.tiles_per_shard =
-        ceil_div(c.q, c.coll == kReduceScatter ? tile_elems<T, RsPolicy>() : tile_elems<T, AgPolicy>());
-    a.ntiles = uint64_t(c.nranks) * a.tiles_per_shard;
-    a.limit = c.limit;
-    const unsigned grid = grid_for(a.ntiles, c.num_cus);
-    if (c.coll == kReduceScatter) {
-      return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
-        hipLaunchKernelGGL((rs_direct_kernel<U, OP>), dim3(grid), dim3(RsPolicy::TB), 0, c.stream, a);
-        return hipGetLastError();
-      });
-    }
-    hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid), dim3(AgPolicy::TB), 0, c.stream, a);
-    return hipGetLastError();
+    const uint64_t produced = (c.coll == kAllReduce) ? c.limit : uint64_t(c.nranks) * c.q;
+    const bool small = produced <= CCL_SIM_DIRECT_SMALL_CALL;
+    return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
+      if (c.coll == kAllReduce)
+        return small ? launch_ar_direct<U, OP, DirectSmallPolicy>(c) : launch_ar_direct<U, OP, ArPolicy>(c);
+      return small ? launch_rs_direct<U, OP, DirectSmallPolicy>(c) : launch_rs_direct<U, OP, RsPolicy>(c);
+    });
   });
 }
 
