@@ -48,11 +48,26 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_digest():
-    """Digest of the device code's source: comments and whitespace are
-    dropped first, so a comment edit does not count as a kernel change."""
+# The source file that holds each kernel; every kernel also depends on the
+# shared device headers.
+KERNEL_FILES = {
+    "rs_direct_kernel": "kernels_direct.hip",
+    "ag_direct_kernel": "kernels_direct.hip",
+    "ar_direct_kernel": "kernels_direct.hip",
+    "ring_step_kernel": "kernels_ring.hip",
+    "ring_persistent_kernel": "kernels_ring.hip",
+    "recursive_step_kernel": "kernels_recursive.hip",
+    "pad_kernel": "kernels_misc.hip",
+}
+
+
+def kernel_source_digest(kernel):
+    """Digest of the device code a kernel is built from: its own source file
+    and the shared headers, with comments and whitespace dropped first, so
+    a comment edit or a change to another kernel's file does not count as a
+    change of this kernel."""
     h = hashlib.sha256()
-    for name in ("kernels.hip", "device.hpp", "internal.hpp"):
+    for name in ("kernel_common.hpp", "device.hpp", "internal.hpp", KERNEL_FILES[kernel]):
         with open(os.path.join(HERE, "collective_reduction_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -72,7 +87,7 @@ def load_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     entry = rec.get(f"{kernel}:{workload}")
-    if not entry or entry.get("source_digest") != kernel_source_digest():
+    if not entry or entry.get("source_digest") != kernel_source_digest(kernel):
         return None
     return entry.get("traffic_bytes")
 
@@ -284,7 +299,7 @@ def main():
         "lifetimes_256MiB_per_rank_world4": lifetimes,
         "cpu_baseline": cpu,
         "device": dev_name,
-        "kernel_source_digest": kernel_source_digest(),
+        "kernel_source_digest": kernel_source_digest(dominant[0]),
     }
     print(json.dumps(out), flush=True)
 
@@ -315,7 +330,8 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
     es = send[0].element_size()
     print(json.dumps({"counters_pass": True, "calls": calls,
                       "copy_read_bytes": n * m * es, "copy_write_bytes": n * m * es,
-                      "kernel_source_digest": kernel_source_digest()}), flush=True)
+                      "kernel_source_digests": {k: kernel_source_digest(k) for k in list(calls) + ["pad_kernel"]}}),
+          flush=True)
 
 
 def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):

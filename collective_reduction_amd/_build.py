@@ -2,21 +2,27 @@
 
     python -m collective_reduction_amd._build [--extra-flag ...]
 
-The library is written next to this file so that it travels with the source
-tree; the binding (``ccl_sim.py``) loads it from there.
+Each source is compiled to an object on its own thread, then the objects
+are linked into the shared library.  The library is written next to this
+file so that it travels with the source tree; the binding (``ccl_sim.py``)
+loads it from there.
 """
 
 import os
 import shlex
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libccl_sim.so")
-SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "model.cpp"), os.path.join(CSRC, "kernels.hip")]
+HOST_SOURCES = ["api.cpp", "model.cpp"]
+KERNEL_SOURCES = ["kernels_direct.hip", "kernels_ring.hip", "kernels_recursive.hip", "kernels_misc.hip"]
+SOURCES = [os.path.join(CSRC, s) for s in HOST_SOURCES + KERNEL_SOURCES]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
@@ -25,7 +31,6 @@ FLAGS = [
     "-O3",
     "-std=c++20",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,10 +39,7 @@ FLAGS = [
 ]
 
 
-def build(extra_flags=(), output=LIB, verbose=False):
-    """Compile every HIP source into ``output``; raises on failure."""
-    tmp = output + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-x", "hip", *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(shlex.quote(c) for c in cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,7 +48,20 @@ def build(extra_flags=(), output=LIB, verbose=False):
     noise = [ln for ln in proc.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, output)
+
+
+def build(extra_flags=(), output=LIB, verbose=False, jobs=None):
+    """Compile every source and link ``output``; raises on failure."""
+    jobs = jobs or min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with tempfile.TemporaryDirectory(prefix="ccl_sim_build_") as tmpdir:
+        objects = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[HIPCC, *FLAGS, *extra_flags, "-x", "hip", "-c", src, "-o", obj] for src, obj in zip(SOURCES, objects)]
+        with ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for cmd in cmds]:
+                f.result()
+        tmp = output + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objects, "-o", tmp], verbose)
+        os.replace(tmp, output)
     return output
 
 

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI front end (api.cpp: validation and
-// planning) and the kernels (kernels.hip: launches).  Not installed.
+// planning) and the kernels (kernels_*.hip: launches).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>

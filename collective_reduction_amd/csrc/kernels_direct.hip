@@ -1,0 +1,204 @@
+// Direct schedule: fused N-way reduce (ReduceScatter), broadcast-copy
+// (AllGather) and fused AllReduce, each reading every input once.
+
+#include "kernel_common.hpp"
+
+namespace ccl {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Direct schedule.
+// ---------------------------------------------------------------------------
+struct ShardArgs {
+  RankPtrs send, recv;
+  int nranks;
+  uint64_t q;                // shard length
+  uint64_t tiles_per_shard;  // ceil(q / tile)
+  uint64_t ntiles;           // nranks · tiles_per_shard
+  uint64_t limit;            // AllGather: recvcount (positions at or past it are trimmed)
+};
+
+// ReduceScatter: recv[r][j] = ⊕_s send[s][r·q + j] ([DECOMP] §数学证明;
+// [RS-PAGE] equation rs-semantic-output).  One pass over the N inputs, one
+// write of the shards: (N+1)·M elements of HBM traffic.
+template <class T, int OP, class P, bool FULL>
+__device__ inline void rs_tile(const ShardArgs& a, int r, uint64_t seg) {
+  using L = Lane<T, P, FULL>;
+  constexpr int V = vec_elems<T>();
+  const L ln(seg, a.q);
+  typename T::A acc[P::U][V];
+  fold_ranks<T, OP, P, FULL>(a.send, a.nranks, uint64_t(r) * a.q, ln, acc);
+  typename T::S* out = out_ptr<T>(a.recv, r);
+#pragma unroll
+  for (int u = 0; u < P::U; ++u)
+    if (ln.on(u)) ln.store(out, u, finish_vec<T, OP, typename L::SV>(acc[u], a.nranks));
+}
+
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void rs_direct_kernel(ShardArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int r = rank_of_tile(tile, a.tiles_per_shard);
+    const uint64_t seg = tile - uint64_t(r) * a.tiles_per_shard;
+    if ((seg + 1) * kTile <= a.q)
+      rs_tile<T, OP, P, true>(a, r, seg);
+    else
+      rs_tile<T, OP, P, false>(a, r, seg);
+  }
+}
+
+// Output fan-out order of the kernels that store one vector into each of
+// the N outputs (the AllGather and the direct AllReduce).  With many ranks
+// the workgroup starting on tile t begins at output t mod N and wraps
+// around, so the workgroups in flight at one moment write into different
+// output buffers instead of all into output 0, then all into output 1.
+// Measured on float32: the AllGather went from 4.3 to 5.3 TB/s at N = 256,
+// 4.6 to 5.35 at N = 128 and 4.7 to 5.0 at N = 64, the direct AllReduce from
+// 4.5 to 5.0 TB/s at N = 256; at N = 8 it made no difference, and the plain
+// order is kept below the threshold.
+#ifndef CCL_SIM_ROTATE_FROM
+#define CCL_SIM_ROTATE_FROM 64
+#endif
+__device__ inline int first_output(uint64_t tile, int nranks) {
+  return nranks >= CCL_SIM_ROTATE_FROM ? int(tile % uint64_t(nranks)) : 0;
+}
+
+// AllGather: recv[r][s·q + j] = send[s][j] for every r, positions below
+// `limit` only ([DECOMP] §数学证明 AllGather, trim of §Contract 实验四).
+// Each shard vector is read once into registers and stored N times.
+template <class T, bool FULL>
+__device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t len, int r0) {
+  using P = AgPolicy;
+  using L = Lane<T, P, FULL>;
+  const L ln(seg, len);
+  const uint64_t base = uint64_t(s) * a.q;
+  const typename T::S* src = in_ptr<T>(a.send, s);
+  typename L::SV v[P::U];
+#pragma unroll
+  for (int u = 0; u < P::U; ++u)
+    if (ln.on(u)) v[u] = ln.load(src, u);
+  for (int k = 0, r = r0; k < a.nranks; ++k, r = (r + 1 == a.nranks) ? 0 : r + 1) {
+    typename T::S* dst = out_ptr<T>(a.recv, r) + base;
+#pragma unroll
+    for (int u = 0; u < P::U; ++u)
+      if (ln.on(u)) ln.store(dst, u, v[u]);
+  }
+}
+
+template <class T>
+__global__ __launch_bounds__(AgPolicy::TB) void ag_direct_kernel(ShardArgs a) {
+  constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int s = rank_of_tile(tile, a.tiles_per_shard);
+    const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
+    const uint64_t base = uint64_t(s) * a.q;
+    const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+    if ((seg + 1) * kTile <= len)
+      ag_tile<T, true>(a, s, seg, len, first_output(tile, a.nranks));
+    else
+      ag_tile<T, false>(a, s, seg, len, first_output(tile, a.nranks));
+  }
+}
+
+struct FlatArgs {
+  RankPtrs send, recv;
+  int nranks;
+  uint64_t count;
+  uint64_t ntiles;
+};
+
+// Direct AllReduce in one kernel: y^(r)_i = ⊕_s x^(s)_i stored to all N
+// outputs ([DECOMP] §数学证明 Direct AllReduce): 2N·M elements of traffic.
+template <class T, int OP, class P, bool FULL>
+__device__ inline void ar_tile(const FlatArgs& a, uint64_t tile) {
+  using L = Lane<T, P, FULL>;
+  constexpr int V = vec_elems<T>();
+  const L ln(tile, a.count);
+  typename T::A acc[P::U][V];
+  fold_ranks<T, OP, P, FULL>(a.send, a.nranks, 0, ln, acc);
+  typename L::SV o[P::U];
+#pragma unroll
+  for (int u = 0; u < P::U; ++u) o[u] = finish_vec<T, OP, typename L::SV>(acc[u], a.nranks);
+  const int r0 = first_output(tile, a.nranks);
+  for (int k = 0, r = r0; k < a.nranks; ++k, r = (r + 1 == a.nranks) ? 0 : r + 1) {
+    typename T::S* dst = out_ptr<T>(a.recv, r);
+#pragma unroll
+    for (int u = 0; u < P::U; ++u)
+      if (ln.on(u)) ln.store(dst, u, o[u]);
+  }
+}
+
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ar_direct_kernel(FlatArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    if ((tile + 1) * kTile <= a.count)
+      ar_tile<T, OP, P, true>(a, tile);
+    else
+      ar_tile<T, OP, P, false>(a, tile);
+  }
+}
+
+}  // namespace
+
+// The fused reductions (ReduceScatter and AllReduce) take two vectors per
+// lane when a call produces at most 2^24 elements per output set (M for
+// the AllReduce, N·q for the ReduceScatter): each lane then keeps twice as
+// many rank loads in flight, which measured 7-9 % faster there (N = 8 at
+// M = 2^24, N = 256 at M = 2^22) and 3 % slower at M = 2^28.  The
+// AllGather keeps one vector per lane at every size.
+#ifndef CCL_SIM_DIRECT_SMALL_CALL
+#define CCL_SIM_DIRECT_SMALL_CALL (uint64_t(1) << 24)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_ar_direct(const Call& c) {
+  FlatArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.count = c.limit;
+  a.ntiles = ceil_div(c.limit, tile_elems<T, P>());
+  hipLaunchKernelGGL((ar_direct_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0, c.stream, a);
+  return hipGetLastError();
+}
+
+template <class P, class T>
+ShardArgs shard_args(const Call& c) {
+  ShardArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.q = c.q;
+  a.tiles_per_shard = ceil_div(c.q, tile_elems<T, P>());
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_shard;
+  a.limit = c.limit;
+  return a;
+}
+
+template <class T, int OP, class P>
+hipError_t launch_rs_direct(const Call& c) {
+  const ShardArgs a = shard_args<P, T>(c);
+  hipLaunchKernelGGL((rs_direct_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0, c.stream, a);
+  return hipGetLastError();
+}
+
+hipError_t run_direct(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    if (c.coll == kAllGather) {
+      const ShardArgs a = shard_args<AgPolicy, T>(c);
+      hipLaunchKernelGGL((ag_direct_kernel<T>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(AgPolicy::TB), 0, c.stream,
+                         a);
+      return hipGetLastError();
+    }
+    const uint64_t produced = (c.coll == kAllReduce) ? c.limit : uint64_t(c.nranks) * c.q;
+    const bool small = produced <= CCL_SIM_DIRECT_SMALL_CALL;
+    return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
+      if (c.coll == kAllReduce)
+        return small ? launch_ar_direct<U, OP, DirectSmallPolicy>(c) : launch_ar_direct<U, OP, ArPolicy>(c);
+      return small ? launch_rs_direct<U, OP, DirectSmallPolicy>(c) : launch_rs_direct<U, OP, RsPolicy>(c);
+    });
+  });
+}
+
+}  // namespace ccl

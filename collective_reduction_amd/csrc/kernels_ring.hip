@@ -1,0 +1,362 @@
+// Ring schedule: one launch per step, or one persistent cooperative kernel
+// with a grid barrier between steps.
+
+#include "kernel_common.hpp"
+
+namespace ccl {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Ring schedule ([RING] §1 and pseudocode; [PRIMS] §五.2-五.3).
+//
+// Global step numbering of one call:
+//   AllReduce      steps 0..N-2 ReduceScatter phase (t = step),
+//                  steps N-1..2N-3 AllGather phase (t = step - (N-1));
+//   ReduceScatter  steps 0..N-2;
+//   AllGather      step 0 places each rank's own shard, steps 1..N-1 copy.
+// Each step is N independent transfers, one per rank; a tile belongs to one
+// rank's transfer.  "Send" and "receive" are HBM reads of the upstream
+// rank's data; the ReduceScatter phase's in-flight partials live in a
+// double buffer P[2][N][q] of accumulators (rank r's slot of step t is read
+// by rank r+1 at step t+1, so two generations are live at once).
+// ---------------------------------------------------------------------------
+struct RingArgs {
+  RankPtrs send, recv;
+  int nranks;
+  int coll;
+  int step;                  // the step a stepwise launch runs
+  int first_step;            // persistent: 1 skips an in-place AllGather's placement
+  uint64_t q;                // chunk length
+  uint64_t limit;            // positions at or past it are padding / trimmed
+  uint64_t tiles_per_chunk;
+  uint64_t ntiles;           // nranks · tiles_per_chunk
+  void* partial;
+  unsigned* ctrl;
+  unsigned spin_limit;
+};
+
+__device__ inline int mod_n(int x, int n) {
+  x %= n;
+  return x < 0 ? x + n : x;
+}
+
+__device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
+  const uint64_t base = uint64_t(c) * a.q;
+  if (base >= a.limit) return 0;
+  return a.limit - base < a.q ? a.limit - base : a.q;
+}
+
+// ReduceScatter step t for rank r: receive chunk c = (r-1-t) from rank r-1
+// and combine the rank's own x^(r) chunk into it (incoming partial on the
+// left, so chunk c folds x^(c), x^(c+1), ...).  At t = 0 the incoming
+// partial is rank r-1's own input; at the last step t = N-2 the completed
+// chunk is stored as output instead of a partial: AllReduce into
+// out_r[chunk c] (the AllGather phase's source: the phase boundary fused
+// in one state machine as in [DECOMP] §源码三), ReduceScatter into
+// recvbufs[c], c = r+1.
+template <class T, int OP, class P, bool FULL>
+__device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len) {
+  using A = typename T::A;
+  using L = Lane<T, P, FULL>;
+  constexpr int V = vec_elems<T>();
+  const int n = a.nranks;
+  const int up = mod_n(r - 1, n);
+  const uint64_t cbase = uint64_t(c) * a.q;
+  const bool last = (t == n - 2);
+  A* part = static_cast<A*>(a.partial);
+  const uint64_t slot = uint64_t(n) * a.q;  // elements per generation
+  const L ln(seg, len);
+  typename L::AV in[P::U];
+  typename L::SV own[P::U];
+  const typename T::S* mine = in_ptr<T>(a.send, r) + cbase;
+  if (t == 0) {
+    const typename T::S* theirs = in_ptr<T>(a.send, up) + cbase;
+#pragma unroll
+    for (int u = 0; u < P::U; ++u)
+      if (ln.on(u)) {
+        const typename L::SV x = ln.load(theirs, u);
+#pragma unroll
+        for (int k = 0; k < V; ++k) in[u][k] = T::widen(x[k]);
+      }
+  } else {
+    const A* theirs = part + uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q;
+#pragma unroll
+    for (int u = 0; u < P::U; ++u)
+      if (ln.on(u)) in[u] = ln.load_acc(theirs, u);
+  }
+#pragma unroll
+  for (int u = 0; u < P::U; ++u)
+    if (ln.on(u)) own[u] = ln.load(mine, u);
+  if (!last) {
+    A* dst = part + uint64_t(t & 1) * slot + uint64_t(r) * a.q;
+#pragma unroll
+    for (int u = 0; u < P::U; ++u) {
+      if (!ln.on(u)) continue;
+      typename L::AV v;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = combine<T, OP>(in[u][k], T::widen(own[u][k]));
+      ln.store_acc(dst, u, v);
+    }
+  } else {
+    typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, r) + cbase : out_ptr<T>(a.recv, c);
+#pragma unroll
+    for (int u = 0; u < P::U; ++u) {
+      if (!ln.on(u)) continue;
+      typename L::SV v;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] = T::narrow(finalize<T, OP>(combine<T, OP>(in[u][k], T::widen(own[u][k])), n));
+      ln.store(dst, u, v);
+    }
+  }
+}
+
+template <class T, int OP, class P>
+__device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
+  const int n = a.nranks;
+  const int r = rank_of_tile(tile, a.tiles_per_chunk);
+  const uint64_t seg = tile - uint64_t(r) * a.tiles_per_chunk;
+  int c;
+  bool reduce = false;
+  const typename T::S* src;
+  if (a.coll != kAllGather && step < n - 1) {
+    // ReduceScatter phase ([PRIMS] §五.2): receive chunk r-1-t.
+    reduce = true;
+    c = mod_n(r - 1 - step, n);
+    src = nullptr;
+  } else if (a.coll == kAllGather && step == 0) {
+    // Stand-alone AllGather: rank r's own shard into its chunk r
+    // (the directCopySend of [DECOMP] §源码四).
+    c = r;
+    src = in_ptr<T>(a.send, r);
+  } else {
+    // AllGather phase ([PRIMS] §五.3): receive chunk c from rank r-1 and
+    // overwrite the local copy.  After the ring ReduceScatter phase rank r
+    // owns chunk r+1, so it receives chunk r-t; a stand-alone AllGather's
+    // rank r owns chunk r and receives chunk r-1-t.
+    const int t = (a.coll == kAllGather) ? step - 1 : step - (n - 1);
+    const int owner = (a.coll == kAllGather) ? 0 : 1;
+    c = mod_n(r + owner - 1 - t, n);
+    src = in_ptr<T>(a.recv, mod_n(r - 1, n)) + uint64_t(c) * a.q;
+  }
+  const uint64_t len = chunk_len(a, c);
+  const bool full = (seg + 1) * kTile <= len;
+  if (reduce) {
+    if (full)
+      ring_rs_tile<T, OP, P, true>(a, step, r, seg, c, len);
+    else
+      ring_rs_tile<T, OP, P, false>(a, step, r, seg, c, len);
+  } else {
+    typename T::S* dst = out_ptr<T>(a.recv, r) + uint64_t(c) * a.q;
+    if (full)
+      copy_tile<T, P, true>(src, dst, seg, len);
+    else
+      copy_tile<T, P, false>(src, dst, seg, len);
+  }
+}
+
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ring_step_kernel(RingArgs a) {
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P>(a, a.step, tile);
+}
+
+// Grid-wide barrier for the persistent ring.  Every workgroup of the grid
+// is co-resident (cooperative launch) and arrives once per barrier.
+//
+// Arrival is two-level: workgroup b counts itself on the counter of group
+// b mod kCtrlGroups (each counter on its own cache line), and the group's
+// last arriver of this barrier adds one arrival to the global counter, so
+// no counter takes more than about gridDim.x / kCtrlGroups atomics per
+// barrier instead of gridDim.x on one address.  Every workgroup then polls
+// the global counter until all groups are in.  Counters only grow, so
+// barrier number `epoch` (from 1) is complete when group g's counter
+// reaches epoch·members(g) and the global counter epoch·groups.
+//
+// Ordering: each wave waits until its own stores have reached its XCD's L2
+// (vmcnt 0) before the workgroup barrier; one lane then issues a release
+// fence at agent scope, which writes that L2's dirty lines back to memory,
+// before arriving.  A group leader fences acquire-release between the
+// group counter and the global counter, which carries its members'
+// releases on; after the wait, an acquire fence drops stale L1 / L2 lines.
+// A workgroup's stores of one step are therefore seen by every other
+// workgroup's loads of the next, across all eight XCDs and their separate
+// L2 caches.  Release and acquire are separate one-way fences: a full
+// fence on each side would write back and invalidate the caches twice.
+//
+// The wait is bounded: after spin_limit polls a workgroup raises the abort
+// word, and every workgroup that sees the word stops, so the grid always
+// drains.
+__device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spin_limit) {
+  __shared__ int s_ok;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned grid = gridDim.x;
+    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
+    const unsigned g = blockIdx.x % unsigned(kCtrlGroups);
+    const unsigned members = (grid - g + kCtrlGroups - 1) / kCtrlGroups;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned before = __hip_atomic_fetch_add(ctrl + kCtrlGroup + g * kCtrlLine, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1u == epoch * members) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int ok = 1;
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch * groups) {
+      if (++spins > spin_limit ||
+          ((spins & 63u) == 0u &&
+           __hip_atomic_load(ctrl + kCtrlAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
+        __hip_atomic_store(ctrl + kCtrlAbort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
+  const int n = a.nranks;
+  const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
+  unsigned epoch = 0;
+  for (int step = a.first_step; step < nsteps; ++step) {
+    if (step > a.first_step && !grid_barrier(a.ctrl, ++epoch, a.spin_limit)) return;
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P>(a, step, tile);
+  }
+}
+
+__global__ void reset_ctrl_kernel(unsigned* ctrl) {
+  for (int i = threadIdx.x; i < kCtrlWords; i += blockDim.x) ctrl[i] = 0u;
+}
+
+RingArgs make_ring_args(const Call& c, uint64_t tile) {
+  RingArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.coll = c.coll;
+  a.q = c.q;
+  a.limit = c.limit;
+  a.tiles_per_chunk = ceil_div(c.q, tile);
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_chunk;
+  a.partial = c.partial;
+  a.ctrl = c.ctrl;
+  a.spin_limit = 1u << 22;
+  return a;
+}
+
+}  // namespace
+
+// Launch shape of the ring step kernels by step size.  A step that moves
+// few elements is over before a one-vector-per-lane grid has ramped up, and
+// two vectors per lane (half the workgroups) measured faster there; large
+// steps are faster with one.  The crossover, measured on float32 with N = 8
+// to 256: a ring step (N chunks of q) of up to 2^26 elements.
+#ifndef CCL_SIM_RING_SMALL_STEP
+#define CCL_SIM_RING_SMALL_STEP (uint64_t(1) << 26)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_ring_steps(const Call& c) {
+  RingArgs a = make_ring_args(c, tile_elems<T, P>());
+  const unsigned grid = grid_for(a.ntiles, c.num_cus);
+  const int n = c.nranks;
+  const int nsteps = (c.coll == kAllReduce) ? 2 * (n - 1) : (c.coll == kReduceScatter ? n - 1 : n);
+  const int first = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  for (int step = first; step < nsteps; ++step) {
+    a.step = step;
+    hipLaunchKernelGGL((ring_step_kernel<T, OP, P>), dim3(grid), dim3(P::TB), 0, c.stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_ring_stepwise(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    const bool small = uint64_t(c.nranks) * c.q <= CCL_SIM_RING_SMALL_STEP;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      return small ? launch_ring_steps<U, OP, RingSmallPolicy>(c) : launch_ring_steps<U, OP, RingPolicy>(c);
+    });
+  });
+}
+
+#ifndef CCL_SIM_PERSISTENT_PER_CU
+#define CCL_SIM_PERSISTENT_PER_CU 1
+#endif
+
+// The persistent grid holds one workgroup per CU (see below), so its lanes
+// alone must keep enough loads in flight.  For steps of up to 2^26
+// elements a 1024-lane workgroup (a step of N = 256 chunks of 2^14 float32
+// is then one tile per workgroup) measured 9-17 % faster than 256 lanes;
+// for larger steps 256 lanes were faster.
+#ifndef CCL_SIM_PERSIST_SMALL_STEP
+#define CCL_SIM_PERSIST_SMALL_STEP (uint64_t(1) << 26)
+#endif
+
+template <class T, int OP, class P>
+hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
+  RingArgs a = make_ring_args(c, tile_elems<T, P>());
+  a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  if (c.spin_limit) a.spin_limit = c.spin_limit;
+  auto kernel = ring_persistent_kernel<T, OP, P>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, P::TB, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu <= 0 || c.num_cus <= 0) {
+    *unsupported = true;
+    return hipSuccess;
+  }
+  // Workgroups per CU: at most what the occupancy calculation allows, and
+  // by default only CCL_SIM_PERSISTENT_PER_CU of them.  A grid at the full
+  // occupancy figure was found not to be co-resident on MI355X (its first
+  // barrier ran into the poll limit); of the grids that are, one workgroup
+  // per CU measured fastest, at every step size: the barrier's cost grows
+  // with the number of workgroups that arrive.
+  const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
+  const int use = want < per_cu ? want : per_cu;
+  uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
+  if (grid > a.ntiles) grid = a.ntiles;
+  if (grid == 0) grid = 1;
+  if (plan) {
+    plan->occupancy_per_cu = per_cu;
+    plan->per_cu = use;
+    plan->grid = grid;
+    plan->tiles_per_step = a.ntiles;
+    plan->lanes = P::TB;
+  }
+  hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void* args[] = {&a};
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)), dim3(P::TB),
+                                 args, 0, c.stream);
+  if (e == hipErrorCooperativeLaunchTooLarge) {
+    (void)hipGetLastError();
+    *unsupported = true;
+    return hipSuccess;
+  }
+  return e;
+}
+
+hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
+  *unsupported = false;
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    const bool small = uint64_t(c.nranks) * c.q <= CCL_SIM_PERSIST_SMALL_STEP;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      return small ? launch_persistent<U, OP, PersistSmallPolicy>(c, unsupported, plan)
+                   : launch_persistent<U, OP, PersistPolicy>(c, unsupported, plan);
+    });
+  });
+}
+
+}  // namespace ccl

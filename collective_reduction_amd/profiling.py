@@ -22,6 +22,7 @@ while that digest still matches.
 import csv
 import json
 import os
+import re
 import sys
 
 
@@ -32,6 +33,13 @@ def _short(name):
         if key in name:
             return key
     return name
+
+
+def _shape(name):
+    """The launch shape a kernel instance was built with (its Policy's lanes
+    per workgroup and vectors per lane), when the name carries one."""
+    m = re.search(r"Policy<(\d+), (\d+),", name)
+    return f" ({m.group(1)} lanes x {m.group(2)} vectors)" if m else ""
 
 
 def stats(stats_csv, out_md, command):
@@ -49,8 +57,8 @@ def stats(stats_csv, out_md, command):
         "|---|---:|---:|---:|---:|---:|",
     ]
     for r in rows:
-        lines.append("| `{}` | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
-            _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        lines.append("| `{}`{} | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            _short(r["Name"]), _shape(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
     lines.append("")
     lines.append("Full kernel names: " + "; ".join(sorted({r["Name"] for r in rows})))
@@ -97,7 +105,7 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
             "fetch_scale": fscale,
             "write_scale": wscale,
             "calibration": "ccl_sim_pad_identity with count == padded_count (plain copy of N*M elements)",
-            "source_digest": info["kernel_source_digest"],
+            "source_digest": info["kernel_source_digests"][kernel],
             "command": command,
         }
     with open(out_json, "w") as f:
@@ -130,8 +138,8 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
         f"factors. Figures are per call, summed over the call's dispatches.",
         "",
         "| call | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B | traffic B "
-        "| algorithmic B | traffic / algorithmic |",
-        "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|",
+        "| algorithmic B | traffic / algorithmic | source digest |",
+        "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---|",
     ]
     for key, r in rec.items():
         kernel = key.split(":")[0]
@@ -139,9 +147,10 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
             f"| {what.get(kernel, kernel)} | `{kernel}` | {r['dispatches']} | {r['fetch_size_kib']:.1f} | "
             f"{r['write_size_kib']:.1f} | {r['read_bytes'] * r['dispatches']:.4e} | "
             f"{r['write_bytes'] * r['dispatches']:.4e} | {r['call_traffic_bytes']:.4e} | "
-            f"{r['call_algorithmic_bytes']:.4e} | {r['traffic_over_algorithmic']:.5f} |")
-    lines += ["", f"Kernel source digest the counters were taken on: `{info['kernel_source_digest']}` (bench.py "
-              "reports `traffic` only while the sources still hash to it)."]
+            f"{r['call_algorithmic_bytes']:.4e} | {r['traffic_over_algorithmic']:.5f} | `{r['source_digest']}` |")
+    lines += ["", "Source digest: the kernel's own source file and the shared device headers, without comments, "
+              "when the counters were taken; bench.py reports a kernel's `traffic` only while its sources still "
+              "hash to it."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
