@@ -9,11 +9,14 @@ float32 each, inputs resident in HBM.  W untimed steps, then K timed steps
 between device synchronisations.  The value is effective HBM bandwidth:
 the schedule's algorithmic bytes 2(N+1)·M·4 divided by the time per step.
 
-Also reported, on the same buffers: per-kernel durations from HIP events on
-the launch stream (the roofline of the dominant kernel), the other
-schedules (ring stepwise / persistent RS+AG, direct and ring AllReduce,
-RS-only), and the CPU oracle timed on a bounded sample of the same
-workload.  Prints exactly one JSON line on stdout; progress goes to stderr.
+Also reported: per-kernel durations from HIP events on the launch stream
+(the roofline of the dominant kernel); on the same buffers, the other
+schedules (ring stepwise / persistent and recursive RS+AG, every
+schedule's AllReduce, RS alone, smaller M), timed in interleaved rounds;
+the 256-rank float32 and bf16 workloads; the alpha-beta model of the same
+payload on two networks; the measured buffer lifetimes; and the CPU oracle
+timed on a bounded sample of the workload.  Prints exactly one JSON line on
+stdout; progress goes to stderr.
 """
 
 import argparse
@@ -39,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="uniform_8x268435456_fp32")
-    p.add_argument("--secondary-iters", type=int, default=5)
+    p.add_argument("--secondary-iters", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle work for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
@@ -334,43 +337,59 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
           flush=True)
 
 
-def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
-    """Other schedules and collectives on the same buffers, each timed with
-    HIP events over `iters` calls after one warm-up call."""
-    res = {}
-    ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
-                               for s in ("ring_stepwise", "ring_persistent", "recursive")])
-
-    def timed(name, fn, nbytes):
+def time_interleaved(torch, stream, cases, iters):
+    """Time every case with HIP events on `stream`: one warm-up call each,
+    then `iters` rounds that run every case once, in forward order in even
+    rounds and reverse order in odd ones, so that no case always follows the
+    same neighbour.  A case that raises is reported, not fatal."""
+    res, live = {}, []
+    for name, fn, nbytes in cases:
         try:
             fn()
             torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-            for a, b in ev:
-                a.record(stream)
-                fn()
-                b.record(stream)
-            torch.cuda.synchronize()
-            ms = [a.elapsed_time(b) for a, b in ev]
-            st = stats(ms)
-            res[name] = {"bytes": nbytes, "gbs": nbytes / (st["median_ms"] / 1e3) / 1e9,
-                         "frac_of_peak": nbytes / (st["median_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, **st}
-            log(f"{name}: {st['median_ms']:.3f} ms, {res[name]['gbs']:.0f} GB/s")
-        except Exception as e:  # a schedule this device cannot run is reported, not fatal
+            live.append((name, fn, nbytes))
+        except Exception as e:  # a schedule this device cannot run
             res[name] = {"error": str(e)}
             log(f"{name}: {e}")
+    ms = {name: [] for name, _, _ in live}
+    for rnd in range(iters):
+        order = live if rnd % 2 == 0 else live[::-1]
+        ev = []
+        for name, fn, _ in order:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((name, a, b))
+        torch.cuda.synchronize()
+        for name, a, b in ev:
+            ms[name].append(a.elapsed_time(b))
+    for name, _, nbytes in live:
+        st = stats(ms[name])
+        gbs = nbytes / (st["median_ms"] / 1e3) / 1e9
+        res[name] = {"bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, **st}
+        log(f"{name}: {st['median_ms']:.3f} ms, {gbs:.0f} GB/s (cv {100 * st['cv']:.1f} %)")
+    return res
 
+
+def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
+    """Other schedules and collectives on the same buffers (every schedule's
+    RS+AG and AllReduce, RS alone, smaller M on prefixes, a plain copy for
+    scale), timed together by time_interleaved."""
+    ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
+                               for s in ("ring_stepwise", "ring_persistent", "recursive")])
     ab = cs.ccl_sim_algorithmic_bytes
+    cases = []
     for sched in ("ring_stepwise", "ring_persistent", "recursive"):
-        timed(f"rs_ag_{sched}", lambda s=sched: (
+        cases.append((f"rs_ag_{sched}", lambda s=sched: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
-            ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched))
+            ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched)))
     for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive"):
-        timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
-            send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
-    timed("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
-          ab("reduce_scatter", n, m, dtype, "direct"))
+        cases.append((f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
+            send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched)))
+    cases.append(("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
+                  ab("reduce_scatter", n, m, dtype, "direct")))
     # smaller M on prefixes of the same buffers (N=8, M = 2^24 and 2^26)
     for lg in (24, 26):
         mm = 1 << lg
@@ -381,19 +400,19 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
         rv = [t[:mm] for t in recv]
         hv = [t[:qq] for t in shards]
         for sched in ("direct", "ring_stepwise"):
-            timed(f"rs_ag_{sched}_m2^{lg}", lambda s=sched, sv=sv, rv=rv, hv=hv, mm=mm, qq=qq: (
+            cases.append((f"rs_ag_{sched}_m2^{lg}", lambda s=sched, sv=sv, rv=rv, hv=hv, mm=mm, qq=qq: (
                 cs.ccl_sim_reduce_scatter(sv, hv, mm, qq, schedule=s, workspace=ws, stream=stream),
                 cs.ccl_sim_all_gather(hv, rv, qq, mm, schedule=s, workspace=ws, stream=stream)),
-                ab("reduce_scatter", n, mm, dtype, sched) + ab("all_gather", n, mm, dtype, sched))
+                ab("reduce_scatter", n, mm, dtype, sched) + ab("all_gather", n, mm, dtype, sched)))
     # plain copy of the same size as one rank's buffer, for scale
-    timed("copy_one_rank_torch", lambda: recv[0].copy_(send[0]), 2 * m * send[0].element_size())
-    return res
+    cases.append(("copy_one_rank_torch", lambda: recv[0].copy_(send[0]), 2 * m * send[0].element_size()))
+    return time_interleaved(torch, stream, cases, iters)
 
 
 def run_many_ranks(cs, torch, stream, iters):
     """The 256-rank workloads (M=2^22 float32; the 6,553,600-element bf16
     bucket) on freshly drawn device buffers: every schedule's AllReduce and
-    the direct RS+AG, timed with HIP events."""
+    the direct RS+AG, timed together by time_interleaved."""
     res = {}
     ab = cs.ccl_sim_algorithmic_bytes
     for name, m, tdt, dtype in (("256x4194304_fp32", 1 << 22, torch.float32, "float32"),
@@ -406,29 +425,15 @@ def run_many_ranks(cs, torch, stream, iters):
         ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
                                    for s in ("direct", "ring_stepwise", "ring_persistent", "recursive")])
         torch.cuda.synchronize()
-
-        def timed(key, fn, nbytes):
-            fn()
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-            for a, b in ev:
-                a.record(stream)
-                fn()
-                b.record(stream)
-            torch.cuda.synchronize()
-            st = stats([a.elapsed_time(b) for a, b in ev])
-            res[f"{key}_{name}"] = {"bytes": nbytes, "gbs": nbytes / (st["median_ms"] / 1e3) / 1e9,
-                                    "frac_of_peak": nbytes / (st["median_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, **st}
-            log(f"{key}_{name}: {st['median_ms']:.3f} ms, {res[f'{key}_{name}']['gbs']:.0f} GB/s")
-
-        for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive"):
-            timed(f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(send, recv, m, schedule=s, workspace=ws,
-                                                                            stream=stream),
-                  ab("allreduce", n, m, dtype, sched))
-        timed("rs_ag_direct", lambda: (cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
-                                       cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),
-              ab("reduce_scatter", n, m, dtype, "direct") + ab("all_gather", n, m, dtype, "direct"))
-        del send, recv, shards, ws
+        cases = [(f"allreduce_{sched}_{name}", lambda s=sched: cs.ccl_sim_allreduce(
+                    send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
+                 for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive")]
+        cases.append((f"rs_ag_direct_{name}", lambda: (
+            cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
+            cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),
+            ab("reduce_scatter", n, m, dtype, "direct") + ab("all_gather", n, m, dtype, "direct")))
+        res.update(time_interleaved(torch, stream, cases, iters))
+        del send, recv, shards, ws, cases
         torch.cuda.empty_cache()
     return res
 
