@@ -1,11 +1,13 @@
 """Turn rocprofv3 output into the short summaries kept under profiles/.
 
     python -m collective_reduction_amd.profiling stats  <kernel_stats.csv> <out.md> <command...>
+    python -m collective_reduction_amd.profiling trace  <kernel_trace.csv> <out.md> <command...>
     python -m collective_reduction_amd.profiling traffic <fetch_counter_collection.csv> \
         <write_counter_collection.csv> <counters_pass_stdout> <workload> <out.json> <out.md>
 
 ``stats`` keeps the per-kernel call count and durations of a
-``--kernel-trace --stats`` run.  ``traffic`` reads two ``--pmc`` runs of
+``--kernel-trace --stats`` run; ``trace`` computes the same from the
+per-dispatch trace, grouped by kernel, launch shape and grid size.  ``traffic`` reads two ``--pmc`` runs of
 ``bench.py --counters-pass`` (FETCH_SIZE, then WRITE_SIZE; KiB per
 dispatch) and scales each counter by what it reads for the plain copy in
 the same pass (``ccl_sim_pad_identity`` with nothing to pad, which reads
@@ -62,6 +64,37 @@ def stats(stats_csv, out_md, command):
             float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e6))
     lines.append("")
     lines.append("Full kernel names: " + "; ".join(sorted({r["Name"] for r in rows})))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def trace(trace_csv, out_md, command):
+    """Per-kernel durations from a --kernel-trace CSV, grouped by kernel,
+    launch shape and grid size, so that launches of one kernel at different
+    sizes (the bench's own step and its secondary runs) stay apart."""
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if r.get("Kind", "KERNEL_DISPATCH") != "KERNEL_DISPATCH":
+            continue
+        name = r["Kernel_Name"]
+        key = (_short(name), _shape(name), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+        ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault(key, []).append(ns)
+    lines = [
+        "# rocprofv3 kernel trace, grouped by kernel and grid",
+        "",
+        "Command (run from `/tmp` with `TMPDIR=/tmp`; `<repo>` is the repository root):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | workgroups | calls | average µs | min µs | max µs | total ms |",
+        "|---|---:|---:|---:|---:|---:|---:|",
+    ]
+    for (kernel, shape, wgs), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{kernel}`{shape} | {wgs} | {len(ns)} | {sum(ns) / len(ns) / 1e3:.1f} | {min(ns) / 1e3:.1f} "
+                     f"| {max(ns) / 1e3:.1f} | {sum(ns) / 1e6:.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -159,6 +192,8 @@ if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif mode == "trace":
+        trace(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif mode == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7],
                 "python -m collective_reduction_amd.profiling " + " ".join(sys.argv[1:]))
