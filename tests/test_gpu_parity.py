@@ -474,3 +474,16 @@ def test_uniform_8x256m_fp32_every_element(cs, schedule):
             _tolerance_ok(want, cols, "float32", n)
     del recv, shards, ar
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_uniform_8x128m_bf16_large_launch_shapes_sampled(cs, schedule):
+    """bf16 above every small-launch threshold (N=8, M=2^27: ring and
+    recursive steps and direct calls of 2^27 elements or more), so each
+    schedule runs its large-step launch shape, and the ring its 32-byte
+    float32 accumulator vectors, on bf16 data: AllReduce and RS+AG on
+    sampled positions."""
+    from collective_reduction_amd import inputs as I
+    s = I.spec("uniform_8x268435456_fp32", count=1 << 27, dtype="bfloat16")
+    _sampled_check(cs, s, schedule, "sum", 1 << 14, 21, coll="allreduce")
+    _sampled_check(cs, s, schedule, "sum", 1 << 14, 22, coll="rs_ag")
