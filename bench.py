@@ -64,14 +64,15 @@ KERNEL_FILES = {
 }
 
 
-def kernel_source_digest(kernel):
+def kernel_source_digest(kernel, csrc=None):
     """Digest of the device code a kernel is built from: its own source file
     and the shared headers, with comments and whitespace dropped first, so
     a comment edit or a change to another kernel's file does not count as a
     change of this kernel."""
+    csrc = csrc or os.path.join(HERE, "collective_reduction_amd", "csrc")
     h = hashlib.sha256()
     for name in ("kernel_common.hpp", "device.hpp", "internal.hpp", KERNEL_FILES[kernel]):
-        with open(os.path.join(HERE, "collective_reduction_amd", "csrc", name), encoding="utf-8") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -79,11 +80,11 @@ def kernel_source_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, path=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
     when none were taken for this kernel and workload or the kernel source
     has changed since."""
-    path = os.path.join(HERE, "profiles", "traffic.json")
+    path = path or os.path.join(HERE, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
