@@ -137,6 +137,12 @@ def cpu_baseline(spec, target_s):
         del xs, shards
     nbytes = 2 * (n + 1) * n * qs * es
     threads = os.environ.get("OMP_NUM_THREADS")
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {
         "value": nbytes / dt / 1e9,
         "unit": "GB/s",
@@ -148,6 +154,7 @@ def cpu_baseline(spec, target_s):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "omp_num_threads": threads,
+        "cpu_model": model,
     }
 
 
