@@ -237,6 +237,50 @@ struct Lane {
   __device__ void store(S* base, int u, SV v) const { store_any<S, SV>(base, u, v); }
   __device__ AV load_acc(const A* base, int u) const { return load_any<A, AV>(base, u); }
   __device__ void store_acc(A* base, int u, AV v) const { store_any<A, AV>(base, u, v); }
+
+  // Accumulators in a scratch buffer that only this kernel's own tiling
+  // reads back (the ring's partials, written at one step and read at the
+  // next with the same chunk geometry and policy).  A 32-byte accumulator
+  // vector (eight float32 of bf16 data) of a whole tile is stored as two
+  // 16-byte halves, each half of every lane side by side, so that one store
+  // instruction covers whole lines and can write through; the tile keeps
+  // its place in the buffer, only the order inside it changes.  Other
+  // vectors, and the tiles that are not whole, use the natural order.
+  static constexpr bool kSplitAcc = FULL && P::ST == kStoreWriteThrough && sizeof(AV) == 32;
+  __device__ AV load_part(const A* base, int u) const {
+    if constexpr (kSplitAcc) {
+      using H = typename VecOf<A, V / 2>::type;
+      const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
+      const H lo = vload<A, V / 2, P::NTL>(half0);
+      const H hi = vload<A, V / 2, P::NTL>(half0 + tile_of<P>(V) / 2);
+      AV v;
+#pragma unroll
+      for (int k = 0; k < V / 2; ++k) {
+        v[k] = lo[k];
+        v[k + V / 2] = hi[k];
+      }
+      return v;
+    } else {
+      return load_acc(base, u);
+    }
+  }
+  __device__ void store_part(A* base, int u, AV v) const {
+    if constexpr (kSplitAcc) {
+      using H = typename VecOf<A, V / 2>::type;
+      H lo, hi;
+#pragma unroll
+      for (int k = 0; k < V / 2; ++k) {
+        lo[k] = v[k];
+        hi[k] = v[k + V / 2];
+      }
+      const uint32_t half_bytes = uint32_t(tile_of<P>(V) / 2 * sizeof(A));
+      const uint32_t off = uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(H)));
+      store_through(base + t0, half_bytes, off, lo);
+      store_through(base + t0 + tile_of<P>(V) / 2, half_bytes, off, hi);
+    } else {
+      store_acc(base, u, v);
+    }
+  }
 };
 
 template <class T>

@@ -82,7 +82,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
     const A* theirs = part + uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q;
 #pragma unroll
     for (int u = 0; u < P::U; ++u)
-      if (ln.on(u)) in[u] = ln.load_acc(theirs, u);
+      if (ln.on(u)) in[u] = ln.load_part(theirs, u);
   }
 #pragma unroll
   for (int u = 0; u < P::U; ++u)
@@ -95,7 +95,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
       typename L::AV v;
 #pragma unroll
       for (int k = 0; k < V; ++k) v[k] = combine<T, OP>(in[u][k], T::widen(own[u][k]));
-      ln.store_acc(dst, u, v);
+      ln.store_part(dst, u, v);
     }
   } else {
     typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, r) + cbase : out_ptr<T>(a.recv, c);
