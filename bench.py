@@ -247,6 +247,8 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic, "kernel": dominant[0],
                 "avg_launch_ms": dominant[1], "algorithmic_bytes_per_launch": dominant[2]}
 
+    step_collective = collective_context(cs, "all_reduce", n, m * send_elem_size, ms_per_step / 1e3)
+
     kernels = {
         "rs_direct_kernel": {"avg_ms": rs_avg, "bytes": bytes_rs, "gbs": bytes_rs / (rs_avg / 1e3) / 1e9,
                              **stats(rs_ms)},
@@ -271,12 +273,15 @@ def main():
             modeled[f"{label}_{algo}"] = cs.ccl_sim_model_estimate("all_reduce", algo, n, m * send_elem_size,
                                                                   alpha_us, beta_gbps)
 
-    lifetimes = None
+    lifetimes = lifetimes_big = None
     if not args.no_secondary:
         from collective_reduction_amd import lifetime as LT
+        # the pages' example (256 MiB per rank, 4 ranks), then the bench's own scale (1 GiB per rank, 8 ranks)
         lifetimes = {mode: LT.measure(mode, 4, 64 << 20, "float32", "direct") for mode in LT.MODES}
-        log("lifetimes (MiB per rank, steady/peak): " + ", ".join(
-            f"{k} {v['steady'] / 2**20:.0f}/{v['peak'] / 2**20:.0f}" for k, v in lifetimes.items()))
+        lifetimes_big = {mode: LT.measure(mode, n, m, dtype, "direct") for mode in LT.MODES}
+        for label, lt in (("256 MiB x 4", lifetimes), (f"{m * send_elem_size >> 20} MiB x {n}", lifetimes_big)):
+            log(f"lifetimes {label} (MiB per rank, steady/peak): " + ", ".join(
+                f"{k} {v['steady'] / 2**20:.0f}/{v['peak'] / 2**20:.0f}" for k, v in lt.items()))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -302,12 +307,14 @@ def main():
                    "bytes_per_step": bytes_step},
         "frac_of_peak": value / PEAK_HBM_GBS,
         "step_stats": stats(step_ms),
+        "collective": step_collective,
         "elements_per_s": n * m / (ms_per_step / 1e3),
         "roofline": roofline,
         "kernels": kernels,
         "secondary": secondary,
         "modeled_context": modeled,
         "lifetimes_256MiB_per_rank_world4": lifetimes,
+        "lifetimes_bench_scale": lifetimes_big,
         "cpu_baseline": cpu,
         "device": dev_name,
         "kernel_source_digest": kernel_source_digest(dominant[0]),
@@ -345,11 +352,26 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
           flush=True)
 
 
-def time_interleaved(torch, stream, cases, iters):
+def collective_context(cs, coll, nranks, payload_bytes, seconds):
+    """nccl-tests style figures for one measured collective of
+    `payload_bytes` per rank ([PRIMS] §七): algbw = payload / time and
+    busbw = algbw x the collective's bus factor, from the measured time on
+    this GPU; and, for context only, the alpha-beta model's time for the same
+    collective between N real ranks on an IB HDR-like link (alpha = 10 us,
+    beta = 25 GB/s, [PRIMS] §四)."""
+    algbw = payload_bytes / seconds / 1e9
+    ring = cs.ccl_sim_model_estimate(coll, "ring", nranks, payload_bytes, 10.0, 25.0)
+    return {"algbw_gbps": algbw, "busbw_gbps": algbw * cs.ccl_sim_busbw_factor(coll, nranks),
+            "modeled_ring_ib_hdr_ms": ring["time_s"] * 1e3}
+
+
+def time_interleaved(torch, stream, cases, iters, context=None):
     """Time every case with HIP events on `stream`: one warm-up call each,
     then `iters` rounds that run every case once, in forward order in even
     rounds and reverse order in odd ones, so that no case always follows the
-    same neighbour.  A case that raises is reported, not fatal."""
+    same neighbour.  A case that raises is reported, not fatal.  `context`
+    maps a case name to (coll, nranks, payload bytes) for the nccl-tests
+    style figures of collective_context."""
     res, live = {}, []
     for name, fn, nbytes in cases:
         try:
@@ -376,6 +398,8 @@ def time_interleaved(torch, stream, cases, iters):
         st = stats(ms[name])
         gbs = nbytes / (st["median_ms"] / 1e3) / 1e9
         res[name] = {"bytes": nbytes, "gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, **st}
+        if context and name in context:
+            res[name]["collective"] = collective_context(*context[name], st["median_ms"] / 1e3)
         log(f"{name}: {st['median_ms']:.3f} ms, {gbs:.0f} GB/s (cv {100 * st['cv']:.1f} %)")
     return res
 
@@ -414,7 +438,15 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
                 ab("reduce_scatter", n, mm, dtype, sched) + ab("all_gather", n, mm, dtype, sched)))
     # plain copy of the same size as one rank's buffer, for scale
     cases.append(("copy_one_rank_torch", lambda: recv[0].copy_(send[0]), 2 * m * send[0].element_size()))
-    return time_interleaved(torch, stream, cases, iters)
+    es = send[0].element_size()
+    context = {}
+    for name, _, _ in cases:
+        if name.startswith("rs_ag_") or name.startswith("allreduce_"):
+            mm = (1 << int(name.rsplit("m2^", 1)[1])) if "_m2^" in name else m
+            context[name] = (cs, "all_reduce", n, mm * es)
+        elif name == "rs_only_direct":
+            context[name] = (cs, "reduce_scatter", n, m * es)
+    return time_interleaved(torch, stream, cases, iters, context)
 
 
 def run_many_ranks(cs, torch, stream, iters):
@@ -440,7 +472,8 @@ def run_many_ranks(cs, torch, stream, iters):
             cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),
             ab("reduce_scatter", n, m, dtype, "direct") + ab("all_gather", n, m, dtype, "direct")))
-        res.update(time_interleaved(torch, stream, cases, iters))
+        context = {c[0]: (cs, "all_reduce", n, m * send[0].element_size()) for c in cases}
+        res.update(time_interleaved(torch, stream, cases, iters, context))
         del send, recv, shards, ws, cases
         torch.cuda.empty_cache()
     return res

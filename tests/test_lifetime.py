@@ -48,3 +48,21 @@ def test_measured_lifetimes_ring(mode):
     want = LT.model(count * 4, n)[mode]
     assert got["steady"] == want["steady"]
     assert want["peak"] <= got["peak"] <= want["peak"] + got["workspace"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", LT.MODES)
+def test_measured_lifetimes_bench_scale(mode):
+    """The same four lifetimes at the bench's scale, 1 GiB per rank over 8
+    virtual ranks: measured steady and peak bytes per rank equal the model
+    (pinned above by the page's table), e.g. 1024 / 2176 MiB for the naive
+    RS + AG and 1024 / 1152 MiB for the optimized one."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    n, count = 8, 1 << 28
+    got = LT.measure(mode, n, count, "float32", "direct")
+    want = LT.model(count * 4, n)[mode]
+    assert got["workspace"] == 0
+    assert got["steady"] == want["steady"]
+    assert got["peak"] == want["peak"]
