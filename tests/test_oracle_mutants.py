@@ -48,6 +48,7 @@ PINS = [
     lambda: P.test_bf16_rounding_cases(),
     lambda: P.test_gradient_like_256_ranks_tolerance(),
     lambda: P.test_avg_is_the_sum_divided_once(),
+    lambda: P.test_normalized_sum_error_by_hand(),
     lambda: Q.test_pair_table_and_volumes(_golden),
     lambda: Q.test_onehot_partials_cover_the_pair_groups(),
     lambda: Q.test_brute_force_integers(),
@@ -169,6 +170,12 @@ def _rd_phase_own_block(bufs, q, record):
     return states
 
 
+def _error_over_abs_of_sum(y, xs, dtype):
+    ref = R.fp64_reference(xs, dtype)
+    got = R.widen(y, dtype).astype(np.float64)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), np.finfo(np.float64).tiny)))
+
+
 _ORIG_FOLD = C.fold
 _ORIG_GATHER = C.all_gather
 _ORIG_COMBINE = R.combine
@@ -191,6 +198,7 @@ MUTANTS = {
     "halving keeps the other half": (H, "kept_range", _kept_range_swapped),
     "halving combines upper rank on the left": (H, "_rh_phase", _rh_phase_upper_left),
     "doubling copies the receiver's own block": (H, "_rd_phase", _rd_phase_own_block),
+    "tolerance measure divides by |sum| instead of sum of |x|": (R, "normalized_sum_error", _error_over_abs_of_sum),
 }
 
 

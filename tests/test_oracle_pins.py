@@ -416,6 +416,21 @@ def test_fp32_ring_vs_ascending_order():
         assert ea <= 1e-5 * n and eb <= 1e-5 * n
 
 
+def test_normalized_sum_error_by_hand():
+    """The tolerance measure on values worked out by hand: the error is
+    |y - Σx| over Σ|x| (not over |Σx|, which a cancelling sum would make
+    tiny), computed in float64, maximised over positions."""
+    xs = [np.array([1.0, 1.0, 0.5], dtype=np.float32), np.array([2.0, -1.0, 0.25], dtype=np.float32)]
+    y = np.array([3.0, 2.0 ** -20, 0.75], dtype=np.float32)
+    # position 0: exact -> 0; position 1: sum 0, |x| sum 2 -> 2^-20 / 2; position 2: exact
+    assert R.normalized_sum_error(y, xs, "float32") == 2.0 ** -21
+    y2 = np.array([3.0 + 2.0 ** -22, 0.0, 0.75], dtype=np.float32)
+    assert R.normalized_sum_error(y2, xs, "float32") == 2.0 ** -22 / 3.0
+    bf = [(x.view(np.uint32) >> 16).astype(np.uint16) for x in xs]
+    yb = (np.array([3.0, 0.0, 0.75], dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert R.normalized_sum_error(yb, bf, "bfloat16") == 0.0
+
+
 def test_avg_is_the_sum_divided_once():
     """AVG = one correctly rounded division of the schedule's float32 sum by
     N (checked against Python's own division of the exact binary32 sum), and
