@@ -59,6 +59,7 @@ KERNEL_FILES = {
     "ar_direct_kernel": "kernels_direct.hip",
     "ring_step_kernel": "kernels_ring.hip",
     "ring_persistent_kernel": "kernels_ring.hip",
+    "ring_chained_kernel": "kernels_ring.hip",
     "recursive_step_kernel": "kernels_recursive.hip",
     "pad_kernel": "kernels_misc.hip",
 }
@@ -336,7 +337,8 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
     calls = {"rs_direct_kernel": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct"),
              "ag_direct_kernel": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")}
     for kernel, schedule in (("ar_direct_kernel", "direct"), ("ring_step_kernel", "ring_stepwise"),
-                             ("ring_persistent_kernel", "ring_persistent"), ("recursive_step_kernel", "recursive")):
+                             ("ring_persistent_kernel", "ring_persistent"), ("ring_chained_kernel", "ring_chained"),
+                             ("recursive_step_kernel", "recursive")):
         if schedule == "recursive" and n & (n - 1):
             continue
         ws = cs.Workspace("allreduce", n, m, dtype, schedule)
@@ -409,15 +411,15 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
     RS+AG and AllReduce, RS alone, smaller M on prefixes, a plain copy for
     scale), timed together by time_interleaved."""
     ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
-                               for s in ("ring_stepwise", "ring_persistent", "recursive")])
+                               for s in ("ring_stepwise", "ring_persistent", "ring_chained", "recursive")])
     ab = cs.ccl_sim_algorithmic_bytes
     cases = []
-    for sched in ("ring_stepwise", "ring_persistent", "recursive"):
+    for sched in ("ring_stepwise", "ring_persistent", "ring_chained", "recursive"):
         cases.append((f"rs_ag_{sched}", lambda s=sched: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
             ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched)))
-    for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive"):
+    for sched in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive"):
         cases.append((f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
             send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched)))
     cases.append(("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
@@ -463,11 +465,11 @@ def run_many_ranks(cs, torch, stream, iters):
         recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
         shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
         ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
-                                   for s in ("direct", "ring_stepwise", "ring_persistent", "recursive")])
+                                   for s in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive")])
         torch.cuda.synchronize()
         cases = [(f"allreduce_{sched}_{name}", lambda s=sched: cs.ccl_sim_allreduce(
                     send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
-                 for sched in ("direct", "ring_stepwise", "ring_persistent", "recursive")]
+                 for sched in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive")]
         cases.append((f"rs_ag_direct_{name}", lambda: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),

@@ -38,7 +38,7 @@ ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
 
 bool valid_dtype(int d) { return d >= CCL_SIM_INT32 && d <= CCL_SIM_BFLOAT16; }
 bool valid_op(int o) { return o >= CCL_SIM_SUM && o <= CCL_SIM_AVG; }
-bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RECURSIVE; }
+bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RING_CHAINED; }
 bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 int log2i(int n) {
   int k = 0;
@@ -77,7 +77,7 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
     l.recv_tab = off + tab;
     off += 2 * tab;
   }
-  const bool ring = sched == CCL_SIM_RING_STEPWISE || sched == CCL_SIM_RING_PERSISTENT;
+  const bool ring = sched == CCL_SIM_RING_STEPWISE || sched == CCL_SIM_RING_PERSISTENT || sched == CCL_SIM_RING_CHAINED;
   const bool halving = sched == CCL_SIM_RECURSIVE;
   if ((ring && nranks >= 3) || (halving && nranks >= 4)) {
     if (coll == CCL_SIM_COLL_ALL_GATHER) {
@@ -85,8 +85,11 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
       return l;
     }
     const uint64_t q = shard_len(m, nranks);
-    // ring: [2][N][q] partials; recursive halving: [N][(N/2)·q] per-rank halves
-    const uint64_t per_q = ring ? uint64_t(2) * uint64_t(nranks) : uint64_t(nranks) * uint64_t(nranks / 2);
+    // ring: [2][N][q] partials (chained ring: [N][q], one per chunk);
+    // recursive halving: [N][(N/2)·q] per-rank halves
+    const uint64_t per_q = sched == CCL_SIM_RING_CHAINED ? uint64_t(nranks)
+                           : ring                          ? uint64_t(2) * uint64_t(nranks)
+                                                           : uint64_t(nranks) * uint64_t(nranks / 2);
     uint64_t bytes = 0;
     if (__builtin_mul_overflow(q, per_q * accum_size(dtype), &bytes) ||
         bytes > SIZE_MAX - off - kAlign) {
@@ -315,6 +318,8 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     e = run_ring_stepwise(c);
   } else if (sched == CCL_SIM_RECURSIVE) {
     e = run_recursive(c);
+  } else if (sched == CCL_SIM_RING_CHAINED) {
+    e = run_ring_chained(c);
   } else {
     bool unsupported = false;
     PersistentPlan plan;
@@ -479,7 +484,7 @@ int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_
   if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS || !valid_sched(schedule)) return -1;
   if (count == 0) return 0;
   const int sched = effective_schedule(nranks, schedule);
-  if (sched == CCL_SIM_DIRECT || sched == CCL_SIM_RING_PERSISTENT) return 1;
+  if (sched == CCL_SIM_DIRECT || sched == CCL_SIM_RING_PERSISTENT || sched == CCL_SIM_RING_CHAINED) return 1;
   if (sched == CCL_SIM_RECURSIVE) {
     if (!pow2(nranks)) return -1;
     const int k = log2i(nranks);

@@ -1,5 +1,6 @@
-// Ring schedule: one launch per step, or one persistent cooperative kernel
-// with a grid barrier between steps.
+// Ring schedule: one launch per step, one persistent cooperative kernel
+// with a grid barrier between steps, or each chunk's steps chained in one
+// launch.
 
 #include "kernel_common.hpp"
 
@@ -18,7 +19,9 @@ namespace {
 // rank's transfer.  "Send" and "receive" are HBM reads of the upstream
 // rank's data; the ReduceScatter phase's in-flight partials live in a
 // double buffer P[2][N][q] of accumulators (rank r's slot of step t is read
-// by rank r+1 at step t+1, so two generations are live at once).
+// by rank r+1 at step t+1, so two generations are live at once), or, for
+// the chained ring, in P[N][q] keyed by chunk (chunk c's partial moves
+// from rank to rank in place; only chunk c's own chain touches it).
 // ---------------------------------------------------------------------------
 struct RingArgs {
   RankPtrs send, recv;
@@ -31,6 +34,7 @@ struct RingArgs {
   uint64_t tiles_per_chunk;
   uint64_t ntiles;           // nranks · tiles_per_chunk
   void* partial;
+  int chunk_keyed;           // partials keyed by chunk (chained ring) instead of [step parity][rank]
   unsigned* ctrl;
   unsigned spin_limit;
 };
@@ -79,7 +83,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
         for (int k = 0; k < V; ++k) in[u][k] = T::widen(x[k]);
       }
   } else {
-    const A* theirs = part + uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q;
+    const A* theirs = part + (a.chunk_keyed ? cbase : uint64_t((t - 1) & 1) * slot + uint64_t(up) * a.q);
 #pragma unroll
     for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) in[u] = ln.load_part(theirs, u);
@@ -88,7 +92,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
   for (int u = 0; u < P::U; ++u)
     if (ln.on(u)) own[u] = ln.load(mine, u);
   if (!last) {
-    A* dst = part + uint64_t(t & 1) * slot + uint64_t(r) * a.q;
+    A* dst = part + (a.chunk_keyed ? cbase : uint64_t(t & 1) * slot + uint64_t(r) * a.q);
 #pragma unroll
     for (int u = 0; u < P::U; ++u) {
       if (!ln.on(u)) continue;
@@ -158,6 +162,36 @@ __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
 template <class T, int OP, class P>
 __global__ __launch_bounds__(P::TB) void ring_step_kernel(RingArgs a) {
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P>(a, a.step, tile);
+}
+
+// The rank that handles chunk c at a global step: the inverse of the chunk
+// a rank handles in ring_body.
+__device__ inline int ring_rank_at(const RingArgs& a, int step, int c) {
+  const int n = a.nranks;
+  if (a.coll != kAllGather && step < n - 1) return mod_n(c + 1 + step, n);  // ReduceScatter phase
+  if (a.coll == kAllGather && step == 0) return c;                          // own-shard placement
+  const int t = (a.coll == kAllGather) ? step - 1 : step - (n - 1);
+  const int owner = (a.coll == kAllGather) ? 0 : 1;
+  return mod_n(c - owner + 1 + t, n);
+}
+
+// Chained ring: work item = (chunk c, tile seg of the chunk).  Each step of
+// the ring moves chunk c from one rank to the next and reads only what the
+// step before wrote for the same chunk and the same positions, so the
+// workgroup that owns an item runs all of its steps in order, each step on
+// the rank ring_body would give it, with the same lane-to-element mapping:
+// every value a step reads was written by the same lane earlier in program
+// order.  No other item touches chunk c's positions, so items need no
+// synchronisation at all.
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void ring_chained_kernel(RingArgs a) {
+  const int nsteps = (a.coll == kAllReduce) ? 2 * (a.nranks - 1) : (a.coll == kReduceScatter ? a.nranks - 1 : a.nranks);
+  for (uint64_t item = blockIdx.x; item < a.ntiles; item += gridDim.x) {
+    const int c = rank_of_tile(item, a.tiles_per_chunk);
+    const uint64_t seg = item - uint64_t(c) * a.tiles_per_chunk;
+    for (int step = a.first_step; step < nsteps; ++step)
+      ring_body<T, OP, P>(a, step, uint64_t(ring_rank_at(a, step, c)) * a.tiles_per_chunk + seg);
+  }
 }
 
 // Grid-wide barrier for the persistent ring.  Every workgroup of the grid
@@ -286,6 +320,23 @@ hipError_t run_ring_stepwise(const Call& c) {
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
       return small ? launch_ring_steps<U, OP, RingSmallPolicy>(c) : launch_ring_steps<U, OP, RingPolicy>(c);
     });
+  });
+}
+
+template <class T, int OP, class P>
+hipError_t launch_ring_chained(const Call& c) {
+  RingArgs a = make_ring_args(c, tile_elems<T, P>());
+  a.first_step = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  a.chunk_keyed = 1;
+  hipLaunchKernelGGL((ring_chained_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0, c.stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t run_ring_chained(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t { return launch_ring_chained<U, OP, RingPolicy>(c); });
   });
 }
 

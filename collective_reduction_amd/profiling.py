@@ -30,7 +30,7 @@ import sys
 
 def _short(name):
     for key in ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
-                "ring_persistent_kernel", "recursive_step_kernel", "pad_kernel", "reset_ctrl_kernel",
+                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "pad_kernel", "reset_ctrl_kernel",
                 "store_table_kernel"):
         if key in name:
             return key
@@ -153,6 +153,7 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
             "ar_direct_kernel": "AllReduce, direct (one kernel)",
             "ring_step_kernel": "AllReduce, stepwise ring (all steps)",
             "ring_persistent_kernel": "AllReduce, persistent ring (one launch)",
+            "ring_chained_kernel": "AllReduce, chained ring (one launch)",
             "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)"}
     lines = [
         f"# HBM traffic of the library's kernels (rocprofv3 counters), {workload}",

@@ -132,7 +132,17 @@ typedef enum {
    * CCL_SIM_UNSUPPORTED).  Block b is reduced as a butterfly: at halving
    * step j ranks i and i XOR N/2^j combine (lower rank's partial) ⊕ (upper
    * rank's partial). */
-  CCL_SIM_RECURSIVE = 3
+  CCL_SIM_RECURSIVE = 3,
+  /* The ring of CCL_SIM_RING_STEPWISE, each chunk's 2(N-1) steps chained in
+   * one launch: a step of chunk c depends only on the step before it of the
+   * same chunk (the recv-reduce-send hand-off between neighbouring ranks of
+   * [RING] §1), so one workgroup follows a slice of chunk c through every
+   * step, with no grid barrier and no relaunch between steps.  Same
+   * routing, same combining order and same algorithmic bytes as the other
+   * ring schedules, bit-identical results.  The partials live in a buffer
+   * keyed by chunk (N·q accumulators), since chunks no longer move in step
+   * lockstep. */
+  CCL_SIM_RING_CHAINED = 4
 } ccl_sim_schedule_t;
 
 typedef enum {
@@ -217,7 +227,8 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
  *   - two pointer tables of 8·N bytes each when nranks > 64;
  *   - the ring's double-buffered partials 2·N·q·a (a = accumulator size: 4
  *     for bf16, else the element size) for ring ReduceScatter and ring
- *     AllReduce with N >= 3;
+ *     AllReduce with N >= 3; N·q·a, one partial per chunk, for the chained
+ *     ring;
  *   - the recursive schedule's per-rank halves N·(N/2)·q·a for its
  *     ReduceScatter and AllReduce with N >= 4.
  * AllGather needs no partials under any schedule.
@@ -250,7 +261,7 @@ uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count
 /* Compute-kernel launches one call enqueues for count > 0: DIRECT 1;
  * stepwise ring N-1 (ReduceScatter), N-1 plus 1 own-shard placement
  * (out-of-place AllGather), 2(N-1) (AllReduce) — the nsteps of [DECOMP]
- * §源码二; persistent ring 1.  Not counted: the pointer-table uploads when
+ * §源码二; persistent and chained ring 1.  Not counted: the pointer-table uploads when
  * nranks > 64 and the persistent ring's barrier reset.  N = 1: 1.
  * Returns -1 for invalid arguments. */
 int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_schedule_t schedule,

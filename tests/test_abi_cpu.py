@@ -141,6 +141,11 @@ def test_workspace_sizes(cs):
     assert ws("allreduce", 256, 1 << 22, "float32", "direct") == 2 * 2048
     assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == 1280 + 4096 + 2 * (1 << 22) * 4
     assert ws("allreduce", 1, 100, "float32", "ring_persistent") == 0
+    # chained ring: one partial per chunk, N x q accumulators
+    assert ws("allreduce", 8, 1 << 20, "float32", "ring_chained") == 8 * (1 << 17) * 4
+    assert ws("reduce_scatter", 8, 1 << 20, "bfloat16", "ring_chained") == 8 * (1 << 17) * 4
+    assert ws("all_gather", 8, 1 << 20, "float32", "ring_chained") == 0
+    assert ws("allreduce", 2, 1000, "float32", "ring_chained") == 0
     assert ws("allreduce", 0, 100, "float32", "direct") == ctypes.c_size_t(-1).value
 
 
@@ -152,6 +157,8 @@ def test_algorithmic_bytes(cs):
     assert ab("allreduce", n, m, "float32", "direct") == 2 * n * m * 4
     assert ab("reduce_scatter", n, m, "float32", "ring_stepwise") == 3 * (n - 1) * m * 4
     assert ab("all_gather", n, m, "float32", "ring_persistent") == 2 * n * m * 4
+    for coll in ("reduce_scatter", "all_gather", "allreduce"):
+        assert ab(coll, n, m, "float32", "ring_chained") == ab(coll, n, m, "float32", "ring_stepwise")
     assert ab("allreduce", n, m, "float32", "ring_stepwise") == 5 * (n - 1) * m * 4
     assert ab("allreduce", 256, 1 << 22, "float32", "ring_stepwise") == 21_390_950_400
     # bf16 with fp32 partials: first step 2+2+4, middle 4+2+4, last 4+2+2 bytes per position
@@ -170,6 +177,8 @@ def test_launch_counts_follow_the_step_counts(cs, golden):
     assert lc("all_gather", 4, 100, "ring_stepwise") == 4
     assert lc("allreduce", 8, 100, "direct") == 1
     assert lc("allreduce", 8, 100, "ring_persistent") == 1
+    assert lc("allreduce", 8, 100, "ring_chained") == 1
+    assert lc("all_gather", 8, 100, "ring_chained") == 1
     assert lc("allreduce", 8, 0, "ring_stepwise") == 0
 
 
