@@ -333,10 +333,31 @@ hipError_t launch_ring_chained(const Call& c) {
   return hipGetLastError();
 }
 
+// Launch shape of the chained ring.  Every item runs 2(N-1) dependent
+// steps, so each lane should keep several loads in flight: two vectors per
+// lane measured best in general (2-6 % over one).  When the chunks are
+// short and few items run long chains (N = 256 chunks of 2^14 float32:
+// 1024 items of 510 steps), four vectors per lane were faster still
+// (3.09 against 3.52 ms), provided the chunk is a whole number of those
+// tiles; a ragged last tile took that gain away on bf16 chunks of 25,600.
+#ifndef CCL_SIM_CHAIN_POLICY
+#define CCL_SIM_CHAIN_POLICY 256, 2, true, kStoreWriteThrough
+#endif
+#ifndef CCL_SIM_CHAIN_LONG_POLICY
+#define CCL_SIM_CHAIN_LONG_POLICY 256, 4, true, kStoreWriteThrough
+#endif
+using ChainPolicy = Policy<CCL_SIM_CHAIN_POLICY>;
+using ChainLongPolicy = Policy<CCL_SIM_CHAIN_LONG_POLICY>;
+
 hipError_t run_ring_chained(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
-    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t { return launch_ring_chained<U, OP, RingPolicy>(c); });
+    const uint64_t long_tile = tile_elems<T, ChainLongPolicy>();
+    const uint64_t long_items = uint64_t(c.nranks) * ceil_div(c.q, long_tile);
+    const bool long_chains = c.q % long_tile == 0 && long_items <= uint64_t(c.num_cus) * 4;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      return long_chains ? launch_ring_chained<U, OP, ChainLongPolicy>(c) : launch_ring_chained<U, OP, ChainPolicy>(c);
+    });
   });
 }
 
