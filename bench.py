@@ -263,6 +263,7 @@ def main():
         del send, shards, recv
         torch.cuda.empty_cache()
         secondary.update(run_many_ranks(cs, torch, stream, args.secondary_iters))
+        secondary.update(run_small(cs, torch, stream))
 
     # Modeled context only (not a measurement, not a target): the pages'
     # α-β model of the same collective between N real ranks on their two
@@ -478,6 +479,52 @@ def run_many_ranks(cs, torch, stream, iters):
         res.update(time_interleaved(torch, stream, cases, iters, context))
         del send, recv, shards, ws, cases
         torch.cuda.empty_cache()
+    return res
+
+
+def run_small(cs, torch, stream, calls=100):
+    """The cache-resident workload (N=8, M=2^20 uniform float32: 32 MiB of
+    inputs, which the 256 MB Infinity Cache holds) and the launch floor.
+    Each figure is the mean over `calls` back-to-back calls between two
+    events, after one warm-up, so the per-call time includes the launch
+    cost: RS+AG with the direct, stepwise-ring and chained-ring schedules,
+    and a 64-element direct AllReduce, which moves almost nothing and so
+    measures what one call costs in launch alone."""
+    from collective_reduction_amd import inputs as I
+    s = I.spec("uniform_8x1048576_fp32")
+    n, m = s["nranks"], s["count"]
+    q = m // n
+    send = [torch.from_numpy(I.rank_buffer(s, r)).to("cuda") for r in range(n)]
+    shards = [torch.empty(q, device="cuda") for _ in range(n)]
+    recv = [torch.empty(m, device="cuda") for _ in range(n)]
+    ab = cs.ccl_sim_algorithmic_bytes
+    ws = cs.Workspace.largest([(c, n, m, "float32", sc) for c in ("reduce_scatter", "all_gather")
+                               for sc in ("ring_stepwise", "ring_chained")])
+    res = {}
+
+    def timed(name, fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(calls):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_ms = a.elapsed_time(b) / calls
+        res[name] = {"bytes": nbytes, "calls": calls, "mean_ms": per_ms, "us_per_call": per_ms * 1e3,
+                     "gbs": nbytes / (per_ms / 1e3) / 1e9 if nbytes else None}
+        log(f"{name}: {per_ms * 1e3:.1f} us per call" + (f", {res[name]['gbs']:.0f} GB/s" if nbytes else ""))
+
+    for sched in ("direct", "ring_stepwise", "ring_chained"):
+        timed(f"rs_ag_{sched}_8x1048576_fp32_cache_resident", lambda sc=sched: (
+            cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=sc, workspace=ws, stream=stream),
+            cs.ccl_sim_all_gather(shards, recv, q, m, schedule=sc, workspace=ws, stream=stream)),
+            ab("reduce_scatter", n, m, "float32", sched) + ab("all_gather", n, m, "float32", sched))
+    tiny_in, tiny_out = [t[:64] for t in send], [t[:64] for t in recv]
+    timed("launch_floor_allreduce_direct_8x64", lambda: cs.ccl_sim_allreduce(tiny_in, tiny_out, 64, stream=stream), 0)
+    del send, shards, recv, ws
+    torch.cuda.empty_cache()
     return res
 
 
