@@ -181,7 +181,9 @@ __device__ inline int ring_rank_at(const RingArgs& a, int step, int c) {
 // workgroup that owns an item runs all of its steps in order, each step on
 // the rank ring_body would give it, with the same lane-to-element mapping:
 // every value a step reads was written by the same lane earlier in program
-// order.  No other item touches chunk c's positions, so items need no
+// order, and a lane's own load after its own store to one address sees the
+// store (the single-thread coherence all GPU code relies on; no fence is
+// involved).  No other item touches chunk c's positions, so items need no
 // synchronisation at all.
 template <class T, int OP, class P>
 __global__ __launch_bounds__(P::TB) void ring_chained_kernel(RingArgs a) {
