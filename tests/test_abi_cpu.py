@@ -236,3 +236,22 @@ def test_recursive_planning(cs):
 def test_result_strings(cs):
     assert cs.ccl_sim_result_string(0) == "success"
     assert cs.ccl_sim_result_string(5) == "capacity mismatch"
+
+
+def test_c_abi_from_plain_c(tmp_path, cs):
+    """include/ccl_sim.h compiles as C11 (with -Wall -Wextra -Werror) and a
+    plain C program linked against the library gets the planning, model and
+    validation results the header states (tests/c/abi_check.c; no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(cs.LIB_PATH)
+    exe = tmp_path / "abi_check"
+    build = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c", "abi_check.c"), "-L", libdir, "-l:" + os.path.basename(cs.LIB_PATH),
+                            "-lm", f"-Wl,-rpath,{libdir}", "-o", str(exe)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
