@@ -489,7 +489,9 @@ def run_small(cs, torch, stream, calls=100):
     events, after one warm-up, so the per-call time includes the launch
     cost: RS+AG with the direct, stepwise-ring and chained-ring schedules,
     and a 64-element direct AllReduce, which moves almost nothing and so
-    measures what one call costs in launch alone."""
+    measures what one call costs in launch alone; then the direct and
+    stepwise-ring RS+AG once more, captured into a HIP graph and replayed,
+    which leaves out the host's per-call work."""
     from collective_reduction_amd import inputs as I
     s = I.spec("uniform_8x1048576_fp32")
     n, m = s["nranks"], s["count"]
@@ -523,6 +525,19 @@ def run_small(cs, torch, stream, calls=100):
             ab("reduce_scatter", n, m, "float32", sched) + ab("all_gather", n, m, "float32", sched))
     tiny_in, tiny_out = [t[:64] for t in send], [t[:64] for t in recv]
     timed("launch_floor_allreduce_direct_8x64", lambda: cs.ccl_sim_allreduce(tiny_in, tiny_out, 64, stream=stream), 0)
+    # the same RS+AG steps captured once into a HIP graph and replayed: no
+    # per-call host work, so what remains is the GPU's own time
+    for sched in ("direct", "ring_stepwise"):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=sched, workspace=ws)
+            cs.ccl_sim_all_gather(shards, recv, q, m, schedule=sched, workspace=ws)
+        torch.cuda.synchronize()
+        timed(f"rs_ag_{sched}_8x1048576_fp32_cache_resident_graph", graph.replay,
+              ab("reduce_scatter", n, m, "float32", sched) + ab("all_gather", n, m, "float32", sched))
+        del graph
     del send, shards, recv, ws
     torch.cuda.empty_cache()
     return res
