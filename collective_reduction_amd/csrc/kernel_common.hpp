@@ -220,13 +220,14 @@ struct Lane {
   }
   template <class E, class EV>
   __device__ void store_any(E* base, int u, EV v) const {
-    if constexpr (FULL && P::ST == kStoreWriteThrough && sizeof(EV) == 16) {
-      store_through(base + t0, uint32_t(tile_of<P>(V) * sizeof(E)),
-                    uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(EV))), v);
-      return;
-    }
     if (whole(u)) {
-      vstore<E, V, P::ST != kStorePlain>(base + j[u], v);
+      // a whole vector, also in the last, ragged tile of a shard: the
+      // resource spans the full tile, but only valid vectors are stored
+      if constexpr (P::ST == kStoreWriteThrough && sizeof(EV) == 16)
+        store_through(base + t0, uint32_t(tile_of<P>(V) * sizeof(E)),
+                      uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(EV))), v);
+      else
+        vstore<E, V, P::ST != kStorePlain>(base + j[u], v);
       return;
     }
 #pragma unroll
