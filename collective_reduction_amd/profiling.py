@@ -34,7 +34,10 @@ def _short(name):
                 "store_table_kernel"):
         if key in name:
             return key
-    return name
+    # another library's kernel (torch's fill and random kernels): its bare
+    # function name, without namespaces, template arguments or parameters
+    head = re.split(r"[<(]", name.replace("(anonymous namespace)", ""), maxsplit=1)[0].split()
+    return head[-1].split("::")[-1] if head else name
 
 
 def _shape(name):
