@@ -196,10 +196,13 @@ struct Lane {
   using SV = typename VecOf<S, V>::type;
   using AV = typename VecOf<A, V>::type;
   uint64_t t0;  // first element of the tile (the same for every lane)
+  uint64_t tv;  // valid elements of the tile from t0 (the tile's size when FULL)
   uint64_t j[U];
   int cnt[U];
 
-  __device__ Lane(uint64_t seg, uint64_t len) : t0(seg * tile_of<P>(V)) {
+  __device__ Lane(uint64_t seg, uint64_t len)
+      : t0(seg * tile_of<P>(V)),
+        tv(FULL ? tile_of<P>(V) : (len > t0 ? (len - t0 < tile_of<P>(V) ? len - t0 : tile_of<P>(V)) : 0)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       j[u] = seg * tile_of<P>(V) + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * V;
@@ -242,45 +245,52 @@ struct Lane {
   // Accumulators in a scratch buffer that only this kernel's own tiling
   // reads back (the ring's partials, written at one step and read at the
   // next with the same chunk geometry and policy).  A 32-byte accumulator
-  // vector (eight float32 of bf16 data) of a whole tile is stored as two
-  // 16-byte halves, each half of every lane side by side, so that one store
-  // instruction covers whole lines and can write through; the tile keeps
-  // its place in the buffer, only the order inside it changes.  Other
-  // vectors, and the tiles that are not whole, use the natural order.
-  static constexpr bool kSplitAcc = FULL && P::ST == kStoreWriteThrough && sizeof(AV) == 32;
+  // vector (eight float32 of bf16 data) is stored as two 16-byte halves,
+  // the first halves of the tile's valid vectors side by side, then the
+  // second halves, so that one store instruction covers whole lines and
+  // can write through; the tile keeps its place in the buffer, only the
+  // order inside it changes.  This holds for every tile whose valid part
+  // is whole vectors (a ragged last tile of a chunk too: its halves then
+  // split its valid part, not the full tile).  Other vectors, and tiles
+  // that end in a partial vector, use the natural order.
+  static constexpr bool kSplitAcc = P::ST == kStoreWriteThrough && sizeof(AV) == 32;
+  __device__ bool split() const { return FULL || tv % V == 0; }
   __device__ AV load_part(const A* base, int u) const {
     if constexpr (kSplitAcc) {
-      using H = typename VecOf<A, V / 2>::type;
-      const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
-      const H lo = vload<A, V / 2, P::NTL>(half0);
-      const H hi = vload<A, V / 2, P::NTL>(half0 + tile_of<P>(V) / 2);
-      AV v;
+      if (split()) {
+        using H = typename VecOf<A, V / 2>::type;
+        const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
+        const H lo = vload<A, V / 2, P::NTL>(half0);
+        const H hi = vload<A, V / 2, P::NTL>(half0 + tv / 2);
+        AV v;
 #pragma unroll
-      for (int k = 0; k < V / 2; ++k) {
-        v[k] = lo[k];
-        v[k + V / 2] = hi[k];
+        for (int k = 0; k < V / 2; ++k) {
+          v[k] = lo[k];
+          v[k + V / 2] = hi[k];
+        }
+        return v;
       }
-      return v;
-    } else {
-      return load_acc(base, u);
     }
+    return load_acc(base, u);
   }
   __device__ void store_part(A* base, int u, AV v) const {
     if constexpr (kSplitAcc) {
-      using H = typename VecOf<A, V / 2>::type;
-      H lo, hi;
+      if (split()) {
+        using H = typename VecOf<A, V / 2>::type;
+        H lo, hi;
 #pragma unroll
-      for (int k = 0; k < V / 2; ++k) {
-        lo[k] = v[k];
-        hi[k] = v[k + V / 2];
+        for (int k = 0; k < V / 2; ++k) {
+          lo[k] = v[k];
+          hi[k] = v[k + V / 2];
+        }
+        const uint32_t half_bytes = uint32_t(tv / 2 * sizeof(A));
+        const uint32_t off = uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(H)));
+        store_through(base + t0, half_bytes, off, lo);
+        store_through(base + t0 + tv / 2, half_bytes, off, hi);
+        return;
       }
-      const uint32_t half_bytes = uint32_t(tile_of<P>(V) / 2 * sizeof(A));
-      const uint32_t off = uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(H)));
-      store_through(base + t0, half_bytes, off, lo);
-      store_through(base + t0 + tile_of<P>(V) / 2, half_bytes, off, hi);
-    } else {
-      store_acc(base, u, v);
     }
+    store_acc(base, u, v);
   }
 };
 
