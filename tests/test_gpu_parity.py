@@ -222,6 +222,28 @@ def test_misaligned_base_addresses(cs, dtype, schedule):
 
 
 @pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_bf16_chunks_with_ragged_last_tiles(cs, schedule):
+    """bf16 chunks whose last tile is ragged: either it ends on an 8-element
+    vector boundary (the ring keeps the tile's float32 partials as two
+    halves of its valid part) or inside a vector (natural order); chunks
+    shorter than one tile, one element past a whole tile, and several tiles
+    plus a remainder; aligned and odd base addresses."""
+    for n in (5, 8):
+        if not runs(schedule, n):
+            continue
+        for q in (8, 904, 4104, 5000, 5003, 25600):
+            for offset in (0, 3):
+                what = f"n={n} q={q} offset={offset}"
+                xs = U.random_inputs(n, n * q, "bfloat16", seed=500 + n * q + offset)
+                got = U.run_ar(cs, xs, "sum", "bfloat16", schedule, offset=offset)
+                assert_all_same(got, oracle_ar(xs, "sum", "bfloat16", schedule)[0], f"AR {what}")
+                got = U.run_rs(cs, xs, q, "max", "bfloat16", schedule, offset=offset)
+                want = oracle_rs(xs, "max", "bfloat16", q, schedule)
+                for r in range(n):
+                    assert U.same_bits(got[r], want[r]), f"RS {what} rank {r}"
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
 def test_in_place_forms(cs, schedule):
     n, q = (6 if runs(schedule, 6) else 8), 1027
     for dtype in ("float32", "bfloat16", "int64"):
@@ -487,3 +509,39 @@ def test_uniform_8x128m_bf16_large_launch_shapes_sampled(cs, schedule):
     s = I.spec("uniform_8x268435456_fp32", count=1 << 27, dtype="bfloat16")
     _sampled_check(cs, s, schedule, "sum", 1 << 14, 21, coll="allreduce")
     _sampled_check(cs, s, schedule, "sum", 1 << 14, 22, coll="rs_ag")
+
+
+@pytest.mark.parametrize("schedule", ["ring_stepwise", "ring_persistent", "ring_chained"])
+def test_ring_large_ragged_steps_every_element(cs, schedule):
+    """N=8 ring steps of about 2^26 float32 (the large-step launch shapes)
+    whose chunks end in a ragged tile under every launch shape (q =
+    8,390,152).  AllReduce of M = 2^26 + 12345 (virtual padding of 7) and
+    RS + AG of the padded length, every element against the oracle's fold
+    of chunk c in the ring's order."""
+    n = 8
+    m = (1 << 26) + 12345
+    q = -(-m // n)
+    xs = U.random_inputs(n, n * q, "float32", seed=31)
+    send = [U.to_dev(x, "float32") for x in xs]
+    ws = cs.Workspace.largest([("allreduce", n, m, "float32", schedule),
+                               ("reduce_scatter", n, n * q, "float32", schedule),
+                               ("all_gather", n, m, "float32", schedule)])
+    ar = [torch.empty(m, dtype=torch.float32, device="cuda") for _ in range(n)]
+    cs.ccl_sim_allreduce([x[:m] for x in send], ar, m, op="sum", schedule=schedule, workspace=ws)
+    shards = [torch.empty(q, dtype=torch.float32, device="cuda") for _ in range(n)]
+    cs.ccl_sim_reduce_scatter(send, shards, n * q, q, op="sum", schedule=schedule, workspace=ws)
+    gathered = [torch.empty(m, dtype=torch.float32, device="cuda") for _ in range(n)]
+    cs.ccl_sim_all_gather(shards, gathered, q, m, schedule=schedule, workspace=ws)
+    torch.cuda.synchronize()
+    del send
+    for c in range(n):
+        cols = [x[c * q:(c + 1) * q] for x in xs]
+        want = R.narrow(C.fold(cols, "sum", "float32", G.chunk_order(n, c)), "float32")
+        assert U.same_bits(U.to_host(shards[c], "float32"), want), f"shard {c}"
+        hi = min((c + 1) * q, m)
+        want_dev = torch.from_numpy(want[:hi - c * q]).cuda().view(torch.int32)
+        for r in range(n):
+            assert torch.equal(ar[r][c * q:hi].view(torch.int32), want_dev), f"allreduce: rank {r}, chunk {c}"
+            assert torch.equal(gathered[r][c * q:hi].view(torch.int32), want_dev), f"gathered: rank {r}, chunk {c}"
+    del ar, shards, gathered
+    torch.cuda.empty_cache()
