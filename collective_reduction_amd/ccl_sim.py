@@ -192,6 +192,29 @@ def _infer_dtype(bufs, dtype):
     raise ValueError("dtype must be given when buffers are raw addresses")
 
 
+def _check_tensors(bufs, need, code, what):
+    """Rank buffers given as tensors must be contiguous device tensors of
+    the call's dtype, on the current device, holding at least `need`
+    elements: the library sees only addresses, and a host address or a
+    short buffer would reach the kernels.  Raw addresses are the caller's
+    responsibility."""
+    names = {v: k for k, v in DTYPES.items()}
+    for r, b in enumerate(bufs):
+        if not isinstance(b, torch.Tensor):
+            continue
+        if b.device.type != "cuda":
+            raise ValueError(f"{what}[{r}] is a {b.device.type} tensor; the library takes device buffers")
+        if b.device.index != torch.cuda.current_device():
+            raise ValueError(f"{what}[{r}] is on {b.device}, not on the current device "
+                             f"cuda:{torch.cuda.current_device()}")
+        if _TORCH_DTYPES.get(b.dtype) != names.get(code):
+            raise ValueError(f"{what}[{r}] has dtype {b.dtype}; the call is {names.get(code, code)}")
+        if not b.is_contiguous():
+            raise ValueError(f"{what}[{r}] is not contiguous")
+        if b.numel() < need:
+            raise ValueError(f"{what}[{r}] holds {b.numel()} elements; the call needs {need}")
+
+
 def _ws(workspace):
     if workspace is None:
         return ctypes.c_void_p(0), 0
@@ -200,6 +223,8 @@ def _ws(workspace):
             return ctypes.c_void_p(0), 0
         workspace = workspace.tensor
     if isinstance(workspace, torch.Tensor):
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("the workspace must be a contiguous device tensor")
         return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     addr, nbytes = workspace
     return ctypes.c_void_p(int(addr)), int(nbytes)
@@ -211,10 +236,13 @@ def ccl_sim_reduce_scatter(sendbufs, recvbufs, sendcount, recvcount, op="sum", s
     n = len(sendbufs)
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
+    code = _infer_dtype(sendbufs, dtype)
+    _check_tensors(sendbufs, sendcount, code, "sendbufs")
+    _check_tensors(recvbufs, recvcount, code, "recvbufs")
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
-    _check(_reduce_scatter(s, r, n, sendcount, recvcount, _infer_dtype(sendbufs, dtype), _enum(OPS, op, "op"),
+    _check(_reduce_scatter(s, r, n, sendcount, recvcount, code, _enum(OPS, op, "op"),
                            _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
 
 
@@ -224,11 +252,14 @@ def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direc
     n = len(sendbufs)
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
+    code = _infer_dtype(sendbufs, dtype)
+    _check_tensors(sendbufs, sendcount, code, "sendbufs")
+    _check_tensors(recvbufs, recvcount, code, "recvbufs")
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
-    _check(_all_gather(s, r, n, sendcount, recvcount, _infer_dtype(sendbufs, dtype),
-                       _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+    _check(_all_gather(s, r, n, sendcount, recvcount, code, _enum(SCHEDULES, schedule, "schedule"), wp, wb,
+                       _stream(stream)))
 
 
 def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", workspace=None, stream=None,
@@ -237,11 +268,14 @@ def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", wo
     n = len(sendbufs)
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
+    code = _infer_dtype(sendbufs, dtype)
+    _check_tensors(sendbufs, count, code, "sendbufs")
+    _check_tensors(recvbufs, count, code, "recvbufs")
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
-    _check(_allreduce(s, r, n, count, _infer_dtype(sendbufs, dtype), _enum(OPS, op, "op"),
-                      _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+    _check(_allreduce(s, r, n, count, code, _enum(OPS, op, "op"), _enum(SCHEDULES, schedule, "schedule"), wp, wb,
+                      _stream(stream)))
 
 
 def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype=None):
@@ -249,10 +283,12 @@ def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype
     n = len(dsts)
     if len(srcs) != n:
         raise ValueError("srcs and dsts must list the same ranks")
+    code = _infer_dtype(dsts, dtype)
+    _check_tensors(srcs, count, code, "srcs")
+    _check_tensors(dsts, padded_count, code, "dsts")
     s, _ks = _ptr_array(srcs)
     d, _kd = _ptr_array(dsts)
-    _check(_pad_identity(s, d, n, count, padded_count, _infer_dtype(dsts, dtype), _enum(OPS, op, "op"),
-                         _stream(stream)))
+    _check(_pad_identity(s, d, n, count, padded_count, code, _enum(OPS, op, "op"), _stream(stream)))
 
 
 def ccl_sim_workspace_size(coll, nranks, count, dtype, schedule):

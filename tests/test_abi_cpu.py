@@ -107,6 +107,19 @@ def test_count_zero_is_a_noop_even_with_null_pointers(cs):
     cs.ccl_sim_pad_identity([0] * 4, [0] * 4, 0, 0, "sum", dtype="int32")
 
 
+def test_binding_rejects_host_tensors(cs):
+    """A host tensor's address would reach the kernels as a device pointer:
+    the binding refuses it before calling the library."""
+    import torch
+    t = [torch.zeros(8) for _ in range(2)]
+    for call in (lambda: cs.ccl_sim_allreduce(t, t, 8),
+                 lambda: cs.ccl_sim_reduce_scatter(t, t, 8, 4),
+                 lambda: cs.ccl_sim_all_gather(t, t, 4, 8),
+                 lambda: cs.ccl_sim_pad_identity(t, t, 4, 8, "max")):
+        with pytest.raises(ValueError, match="device buffers"):
+            call()
+
+
 def test_in_place_forms_pass_validation_overlap(cs):
     """The in-place forms are accepted by the overlap check (the call then
     fails only at the first HIP call when no GPU is present)."""

@@ -310,6 +310,35 @@ def test_pad_rs_ag_trim(cs, schedule, dtype, op, ident_bits):
     assert_all_same(out, oracle_ar(xs, op, dtype, schedule)[0], "pad+RS+AG vs AR")
 
 
+def test_binding_checks_tensor_arguments(cs):
+    """Tensors that are too short for the counts, of another dtype, not
+    contiguous or on the host are refused before the library is called, and
+    the outputs stay untouched."""
+    n, m = 4, 1000
+    send = [torch.ones(m, device="cuda") for _ in range(n)]
+    recv = [torch.full((m,), 7.0, device="cuda") for _ in range(n)]
+    short = [torch.full((m - 1,), 7.0, device="cuda") for _ in range(n)]
+    with pytest.raises(ValueError, match="holds 999 elements"):
+        cs.ccl_sim_allreduce(send, short, m)
+    with pytest.raises(ValueError, match="dtype"):
+        cs.ccl_sim_allreduce(send, [x.to(torch.int32) for x in recv], m)
+    with pytest.raises(ValueError, match="dtype"):
+        cs.ccl_sim_allreduce(send, recv, m, dtype="bfloat16")
+    strided = [torch.empty(2 * m, device="cuda")[::2] for _ in range(n)]
+    with pytest.raises(ValueError, match="contiguous"):
+        cs.ccl_sim_allreduce(send, strided, m)
+    with pytest.raises(ValueError, match="device buffers"):
+        cs.ccl_sim_allreduce(send, [x.cpu() for x in recv], m)
+    with pytest.raises(ValueError, match="holds"):
+        cs.ccl_sim_reduce_scatter(send, [x[:200] for x in recv], m, 250)
+    torch.cuda.synchronize()
+    for x in recv + short:
+        assert bool((x == 7.0).all())
+    cs.ccl_sim_allreduce(send, recv, m)
+    torch.cuda.synchronize()
+    assert all(bool((x == float(n)).all()) for x in recv)
+
+
 def test_pad_in_place_fills_only_the_tail(cs):
     n, m, p = 3, 1000, 1024
     xs = U.random_inputs(n, p, "float32", seed=3)
