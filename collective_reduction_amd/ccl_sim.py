@@ -192,27 +192,42 @@ def _infer_dtype(bufs, dtype):
     raise ValueError("dtype must be given when buffers are raw addresses")
 
 
-def _check_tensors(bufs, need, code, what):
+_CODE_NAMES = {v: k for k, v in DTYPES.items()}
+_CODE_TORCH = {DTYPES[name]: dt for dt, name in _TORCH_DTYPES.items()}
+
+
+def _refuse(b, r, need, code, what, dev):
+    if b.device.type != "cuda":
+        raise ValueError(f"{what}[{r}] is a {b.device.type} tensor; the library takes device buffers")
+    if b.get_device() != dev:
+        raise ValueError(f"{what}[{r}] is on {b.device}, not on the current device cuda:{dev}")
+    if b.dtype is not _CODE_TORCH.get(code):
+        raise ValueError(f"{what}[{r}] has dtype {b.dtype}; the call is {_CODE_NAMES.get(code, code)}")
+    if not b.is_contiguous():
+        raise ValueError(f"{what}[{r}] is not contiguous")
+    raise ValueError(f"{what}[{r}] holds {b.numel()} elements; the call needs {need}")
+
+
+def _check_tensors(bufs, need, code, what, dev=None):
     """Rank buffers given as tensors must be contiguous device tensors of
     the call's dtype, on the current device, holding at least `need`
     elements: the library sees only addresses, and a host address or a
     short buffer would reach the kernels.  Raw addresses are the caller's
-    responsibility."""
-    names = {v: k for k, v in DTYPES.items()}
+    responsibility.  Returns the current device once it has been read, so a
+    call reads it at most once (the checks run on every call, so they keep
+    to a few cheap tensor attributes)."""
+    want = _CODE_TORCH.get(code)
     for r, b in enumerate(bufs):
         if not isinstance(b, torch.Tensor):
             continue
-        if b.device.type != "cuda":
-            raise ValueError(f"{what}[{r}] is a {b.device.type} tensor; the library takes device buffers")
-        if b.device.index != torch.cuda.current_device():
-            raise ValueError(f"{what}[{r}] is on {b.device}, not on the current device "
-                             f"cuda:{torch.cuda.current_device()}")
-        if _TORCH_DTYPES.get(b.dtype) != names.get(code):
-            raise ValueError(f"{what}[{r}] has dtype {b.dtype}; the call is {names.get(code, code)}")
-        if not b.is_contiguous():
-            raise ValueError(f"{what}[{r}] is not contiguous")
-        if b.numel() < need:
-            raise ValueError(f"{what}[{r}] holds {b.numel()} elements; the call needs {need}")
+        d = b.get_device()
+        if d < 0:
+            _refuse(b, r, need, code, what, dev)
+        if dev is None:
+            dev = torch.cuda.current_device()
+        if d != dev or b.dtype is not want or b.numel() < need or not b.is_contiguous():
+            _refuse(b, r, need, code, what, dev)
+    return dev
 
 
 def _ws(workspace):
@@ -237,8 +252,7 @@ def ccl_sim_reduce_scatter(sendbufs, recvbufs, sendcount, recvcount, op="sum", s
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(sendbufs, sendcount, code, "sendbufs")
-    _check_tensors(recvbufs, recvcount, code, "recvbufs")
+    _check_tensors(recvbufs, recvcount, code, "recvbufs", _check_tensors(sendbufs, sendcount, code, "sendbufs"))
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
@@ -253,8 +267,7 @@ def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direc
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(sendbufs, sendcount, code, "sendbufs")
-    _check_tensors(recvbufs, recvcount, code, "recvbufs")
+    _check_tensors(recvbufs, recvcount, code, "recvbufs", _check_tensors(sendbufs, sendcount, code, "sendbufs"))
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
@@ -269,8 +282,7 @@ def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", wo
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(sendbufs, count, code, "sendbufs")
-    _check_tensors(recvbufs, count, code, "recvbufs")
+    _check_tensors(recvbufs, count, code, "recvbufs", _check_tensors(sendbufs, count, code, "sendbufs"))
     s, _ks = _ptr_array(sendbufs)
     r, _kr = _ptr_array(recvbufs)
     wp, wb = _ws(workspace)
@@ -284,8 +296,7 @@ def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype
     if len(srcs) != n:
         raise ValueError("srcs and dsts must list the same ranks")
     code = _infer_dtype(dsts, dtype)
-    _check_tensors(srcs, count, code, "srcs")
-    _check_tensors(dsts, padded_count, code, "dsts")
+    _check_tensors(dsts, padded_count, code, "dsts", _check_tensors(srcs, count, code, "srcs"))
     s, _ks = _ptr_array(srcs)
     d, _kd = _ptr_array(dsts)
     _check(_pad_identity(s, d, n, count, padded_count, code, _enum(OPS, op, "op"), _stream(stream)))
