@@ -61,6 +61,7 @@ KERNEL_FILES = {
     "ring_persistent_kernel": "kernels_ring.hip",
     "ring_chained_kernel": "kernels_ring.hip",
     "recursive_step_kernel": "kernels_recursive.hip",
+    "recursive_chained_kernel": "kernels_recursive.hip",
     "pad_kernel": "kernels_misc.hip",
 }
 
@@ -329,8 +330,9 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
     direct ReduceScatter and AllGather, ccl_sim_pad_identity with nothing to
     pad (a plain copy of N·M elements, reading and writing N·M·s bytes,
     which calibrates FETCH_SIZE / WRITE_SIZE against a known byte count),
-    then one AllReduce each with the direct, stepwise-ring, persistent-ring
-    and recursive schedules (recursive only for a power-of-two N)."""
+    then one AllReduce each with the direct, stepwise-ring, persistent-ring,
+    chained-ring and both recursive schedules (recursive only for a
+    power-of-two N)."""
     ws = cs.Workspace.largest([("reduce_scatter", n, m, dtype, "direct"), ("all_gather", n, m, dtype, "direct")])
     cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", workspace=ws, stream=stream)
     cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", workspace=ws, stream=stream)
@@ -339,8 +341,9 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
              "ag_direct_kernel": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")}
     for kernel, schedule in (("ar_direct_kernel", "direct"), ("ring_step_kernel", "ring_stepwise"),
                              ("ring_persistent_kernel", "ring_persistent"), ("ring_chained_kernel", "ring_chained"),
-                             ("recursive_step_kernel", "recursive")):
-        if schedule == "recursive" and n & (n - 1):
+                             ("recursive_step_kernel", "recursive"),
+                             ("recursive_chained_kernel", "recursive_chained")):
+        if schedule.startswith("recursive") and n & (n - 1):
             continue
         ws = cs.Workspace("allreduce", n, m, dtype, schedule)
         cs.ccl_sim_allreduce(send, recv, m, schedule=schedule, workspace=ws, stream=stream)
@@ -407,20 +410,23 @@ def time_interleaved(torch, stream, cases, iters, context=None):
     return res
 
 
+RING_AND_RECURSIVE = ("ring_stepwise", "ring_persistent", "ring_chained", "recursive", "recursive_chained")
+
+
 def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
     """Other schedules and collectives on the same buffers (every schedule's
     RS+AG and AllReduce, RS alone, smaller M on prefixes, a plain copy for
     scale), timed together by time_interleaved."""
     ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "all_gather", "allreduce")
-                               for s in ("ring_stepwise", "ring_persistent", "ring_chained", "recursive")])
+                               for s in RING_AND_RECURSIVE])
     ab = cs.ccl_sim_algorithmic_bytes
     cases = []
-    for sched in ("ring_stepwise", "ring_persistent", "ring_chained", "recursive"):
+    for sched in RING_AND_RECURSIVE:
         cases.append((f"rs_ag_{sched}", lambda s=sched: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
             ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched)))
-    for sched in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive"):
+    for sched in ("direct",) + RING_AND_RECURSIVE:
         cases.append((f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
             send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched)))
     cases.append(("rs_only_direct", lambda: cs.ccl_sim_reduce_scatter(send, shards, m, q, stream=stream),
@@ -466,11 +472,11 @@ def run_many_ranks(cs, torch, stream, iters):
         recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
         shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
         ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
-                                   for s in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive")])
+                                   for s in ("direct",) + RING_AND_RECURSIVE])
         torch.cuda.synchronize()
         cases = [(f"allreduce_{sched}_{name}", lambda s=sched: cs.ccl_sim_allreduce(
                     send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
-                 for sched in ("direct", "ring_stepwise", "ring_persistent", "ring_chained", "recursive")]
+                 for sched in ("direct",) + RING_AND_RECURSIVE]
         cases.append((f"rs_ag_direct_{name}", lambda: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),

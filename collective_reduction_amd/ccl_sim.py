@@ -48,7 +48,8 @@ if len(_hip_runtimes_mapped()) > 1:
 SUCCESS, INVALID_ARGUMENT, UNSUPPORTED, INSUFFICIENT_WORKSPACE, HIP_ERROR, CAPACITY_MISMATCH = range(6)
 DTYPES = {"int32": 0, "int64": 1, "float32": 2, "bfloat16": 3}
 OPS = {"sum": 0, "prod": 1, "max": 2, "min": 3, "avg": 4}
-SCHEDULES = {"direct": 0, "ring_stepwise": 1, "ring_persistent": 2, "recursive": 3, "ring_chained": 4}
+SCHEDULES = {"direct": 0, "ring_stepwise": 1, "ring_persistent": 2, "recursive": 3, "ring_chained": 4,
+             "recursive_chained": 5}
 COLLS = {"reduce_scatter": 0, "all_gather": 1, "allreduce": 2}
 INLINE_RANKS = 64
 MAX_RANKS = 1024

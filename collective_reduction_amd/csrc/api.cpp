@@ -38,7 +38,8 @@ ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
 
 bool valid_dtype(int d) { return d >= CCL_SIM_INT32 && d <= CCL_SIM_BFLOAT16; }
 bool valid_op(int o) { return o >= CCL_SIM_SUM && o <= CCL_SIM_AVG; }
-bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RING_CHAINED; }
+bool valid_sched(int s) { return s >= CCL_SIM_DIRECT && s <= CCL_SIM_RECURSIVE_CHAINED; }
+bool recursive(int s) { return s == CCL_SIM_RECURSIVE || s == CCL_SIM_RECURSIVE_CHAINED; }
 bool pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 int log2i(int n) {
   int k = 0;
@@ -78,7 +79,7 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
     off += 2 * tab;
   }
   const bool ring = sched == CCL_SIM_RING_STEPWISE || sched == CCL_SIM_RING_PERSISTENT || sched == CCL_SIM_RING_CHAINED;
-  const bool halving = sched == CCL_SIM_RECURSIVE;
+  const bool halving = recursive(sched);
   if ((ring && nranks >= 3) || (halving && nranks >= 4)) {
     if (coll == CCL_SIM_COLL_ALL_GATHER) {
       l.total = off;
@@ -204,7 +205,7 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", dtype);
   if (coll != CCL_SIM_COLL_ALL_GATHER && !valid_op(op)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid op %d", op);
   if (!valid_sched(schedule)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid schedule %d", schedule);
-  if (schedule == CCL_SIM_RECURSIVE && !pow2(nranks))
+  if (recursive(schedule) && !pow2(nranks))
     return fail(CCL_SIM_UNSUPPORTED, "the recursive halving schedule needs a power-of-two nranks (got %d)", nranks);
   const size_t es = elem_size(dtype);
 
@@ -320,6 +321,8 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     e = run_recursive(c);
   } else if (sched == CCL_SIM_RING_CHAINED) {
     e = run_ring_chained(c);
+  } else if (sched == CCL_SIM_RECURSIVE_CHAINED) {
+    e = run_recursive_chained(c);
   } else {
     bool unsupported = false;
     PersistentPlan plan;
@@ -451,7 +454,7 @@ uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count
     return (n + 1) * m * s;
   }
   if (coll == CCL_SIM_COLL_ALL_GATHER) return 2 * n * m * s;
-  if (sched == CCL_SIM_RECURSIVE) {
+  if (recursive(sched)) {
     if (!pow2(nranks)) return 0;
     // halving step j: every position is reduced by N/2^j ranks, each reading
     // two partials (the inputs at step 1) and writing one (the output at the
@@ -484,6 +487,7 @@ int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_
   if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS || !valid_sched(schedule)) return -1;
   if (count == 0) return 0;
   const int sched = effective_schedule(nranks, schedule);
+  if (sched == CCL_SIM_RECURSIVE_CHAINED) return pow2(nranks) ? 1 : -1;
   if (sched == CCL_SIM_DIRECT || sched == CCL_SIM_RING_PERSISTENT || sched == CCL_SIM_RING_CHAINED) return 1;
   if (sched == CCL_SIM_RECURSIVE) {
     if (!pow2(nranks)) return -1;

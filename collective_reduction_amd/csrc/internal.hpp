@@ -11,7 +11,7 @@ namespace ccl {
 
 enum Coll : int { kReduceScatter = 0, kAllGather = 1, kAllReduce = 2 };
 enum DT : int { kInt32 = 0, kInt64 = 1, kFloat32 = 2, kBFloat16 = 3 };
-enum Sched : int { kDirect = 0, kRingStepwise = 1, kRingPersistent = 2, kRecursive = 3, kRingChained = 4 };
+enum Sched : int { kDirect = 0, kRingStepwise = 1, kRingPersistent = 2, kRecursive = 3, kRingChained = 4, kRecursiveChained = 5 };
 
 // Everything a launch needs, already validated.
 struct Call {
@@ -59,6 +59,7 @@ hipError_t run_ring_stepwise(const Call& c);
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan);
 hipError_t run_recursive(const Call& c);
 hipError_t run_ring_chained(const Call& c);
+hipError_t run_recursive_chained(const Call& c);
 hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded);
 // Copy `n` host-side pointers into a device table on the stream (kernel
 // arguments carry them; no host-to-device memcpy).

@@ -33,6 +33,7 @@ struct RecArgs {
   int phase;                 // 0 halving, 1 doubling, 2 placement
   int step;                  // halving: j (1-based); doubling: t
   int last;                  // halving: this is step k
+  int placed;                // chained AllGather: the own shards are in place already
   uint64_t q;
   uint64_t limit;            // positions at or past it are padding / trimmed
   uint64_t len;              // elements each rank moves in this step
@@ -41,13 +42,19 @@ struct RecArgs {
   void* scratch;
 };
 
-template <class T, int OP, class P, bool FULL>
-__device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint64_t base, uint64_t cnt) {
+// Halving step `step` for rank i over the tile `seg` of the range that
+// starts at position `base` (cnt valid positions from base).  SAME_TILING:
+// every step that touches these partials uses this same tile geometry (the
+// chained driver), so they may take the Lane's split partial order; the
+// stepwise driver re-tiles each step and keeps the natural order.
+template <class T, int OP, class P, bool FULL, bool SAME_TILING>
+__device__ inline void halving_tile(const RecArgs& a, int step, bool last, int i, uint64_t seg, uint64_t base,
+                                    uint64_t cnt) {
   using A = typename T::A;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
   const int n = a.nranks;
-  const int d = n >> a.step;
+  const int d = n >> step;
   const int p = i ^ d;
   const int lo = i < p ? i : p, up = i < p ? p : i;
   const uint64_t half = uint64_t(n / 2) * a.q;           // W_i length
@@ -55,7 +62,7 @@ __device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint6
   A* w = static_cast<A*>(a.scratch);
   const L ln(seg, cnt);
   typename L::AV vl[P::U], vu[P::U];
-  if (a.step == 1) {
+  if (step == 1) {
     const typename T::S* xl = in_ptr<T>(a.send, lo) + base;
     const typename T::S* xu = in_ptr<T>(a.send, up) + base;
 #pragma unroll
@@ -74,11 +81,16 @@ __device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint6
 #pragma unroll
     for (int u = 0; u < P::U; ++u)
       if (ln.on(u)) {
-        vl[u] = ln.load_acc(wl, u);
-        vu[u] = ln.load_acc(wu, u);
+        if constexpr (SAME_TILING) {
+          vl[u] = ln.load_part(wl, u);
+          vu[u] = ln.load_part(wu, u);
+        } else {
+          vl[u] = ln.load_acc(wl, u);
+          vu[u] = ln.load_acc(wu, u);
+        }
       }
   }
-  if (!a.last) {
+  if (!last) {
     A* dst = w + uint64_t(i) * half + (base - base1);
 #pragma unroll
     for (int u = 0; u < P::U; ++u) {
@@ -86,7 +98,10 @@ __device__ inline void halving_tile(const RecArgs& a, int i, uint64_t seg, uint6
       typename L::AV v;
 #pragma unroll
       for (int k = 0; k < V; ++k) v[k] = combine<T, OP>(vl[u][k], vu[u][k]);
-      ln.store_acc(dst, u, v);
+      if constexpr (SAME_TILING)
+        ln.store_part(dst, u, v);
+      else
+        ln.store_acc(dst, u, v);
     }
   } else {
     typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, i) + base : out_ptr<T>(a.recv, i);
@@ -124,9 +139,9 @@ __global__ __launch_bounds__(P::TB) void recursive_step_kernel(RecArgs a) {
     const bool full = (seg + 1) * kTile <= cnt;
     if (a.phase == 0) {
       if (full)
-        halving_tile<T, OP, P, true>(a, i, seg, base, cnt);
+        halving_tile<T, OP, P, true, false>(a, a.step, a.last != 0, i, seg, base, cnt);
       else
-        halving_tile<T, OP, P, false>(a, i, seg, base, cnt);
+        halving_tile<T, OP, P, false, false>(a, a.step, a.last != 0, i, seg, base, cnt);
     } else {
       typename T::S* dst = out_ptr<T>(a.recv, i) + base;
       if (full)
@@ -134,6 +149,83 @@ __global__ __launch_bounds__(P::TB) void recursive_step_kernel(RecArgs a) {
       else
         copy_tile<T, P, false>(src, dst, seg, cnt);
     }
+  }
+}
+
+// Chained driver: work item = (block b, tile seg of the block).  Each
+// position's reduction is its own butterfly over the ranks: at halving step
+// j the ranks that hold block b are those whose top j bits equal b's, and
+// each pairs with the rank that differs in bit N/2^j; at doubling step t
+// block b moves from each rank p with p >> t == b >> t to p XOR 2^t.  A
+// step of block b reads only what earlier steps of block b wrote, at the
+// same positions, so one workgroup runs all of its item's combines and
+// copies, with the same lane-to-element mapping throughout; each value it
+// reads it wrote itself earlier in program order (single-thread coherence;
+// no fence).  Items touch disjoint positions and need no synchronisation.
+// Same pairs, same combining order and same bytes as the stepwise driver.
+//
+// Order inside an item: the halving steps of block b form a binary tree
+// (the node of rank i at step j combines the nodes of ranks i and
+// i XOR N/2^j at step j-1), and the doubling steps a broadcast tree from
+// rank b.  Both are walked depth first rather than step by step, so a
+// partial is read back soon after it was written, while it is still in the
+// caches; with N/2 combines per step at N = 256 a step-by-step walk would
+// leave each item megabytes of partials between write and read.  A node's
+// operands are the same in either order, so the results are too.
+//   Halving: the step-1 nodes are taken in bit-reversed order of their low
+//   bits, which makes the two children of every node consecutive, and a
+//   node is combined as soon as its second child is (a binary counter).
+//   Doubling: rank b XOR bitrev(c) for c = 1 .. N-1 receives from the rank
+//   that differs from it in the top bit of bitrev(c), which c with its
+//   lowest set bit cleared has already filled.
+__device__ inline int bit_reverse(int v, int bits) {
+  return bits == 0 ? 0 : static_cast<int>(__builtin_bitreverse32(static_cast<unsigned>(v)) >> (32 - bits));
+}
+
+template <class T, int OP, class P, bool FULL>
+__device__ inline void recursive_item(const RecArgs& a, int b, uint64_t seg, uint64_t cnt) {
+  const int n = a.nranks;
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  const uint64_t base = uint64_t(b) * a.q;
+  if (a.coll != kAllGather) {
+    for (int c = 0; c < (n >> 1); ++c) {
+      int j = 1, v = c;
+      for (;;) {
+        const int d = n >> j;  // ranks holding block b after step j: top j bits of b, any low bits
+        halving_tile<T, OP, P, FULL, true>(a, j, j == k, (b & ~(d - 1)) | bit_reverse(v, k - j), seg, base, cnt);
+        if (!(v & 1)) break;   // the parent's other child is still to come
+        v >>= 1;
+        ++j;
+      }
+    }
+  } else if (!a.placed) {
+    // stand-alone AllGather, out of place: rank b places its own shard
+    copy_tile<T, P, FULL>(in_ptr<T>(a.send, b), out_ptr<T>(a.recv, b) + base, seg, cnt);
+  }
+  if (a.coll != kReduceScatter) {
+    for (int c = 1; c < n; ++c) {
+      const int x = bit_reverse(c, k);
+      const int i = b ^ x;
+      const int from = i ^ (1 << (31 - __builtin_clz(static_cast<unsigned>(x))));  // doubling step t = top bit of x
+      copy_tile<T, P, FULL>(out_ptr<T>(a.recv, from) + base, out_ptr<T>(a.recv, i) + base, seg, cnt);
+    }
+  }
+}
+
+template <class T, int OP, class P>
+__global__ __launch_bounds__(P::TB) void recursive_chained_kernel(RecArgs a) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
+  for (uint64_t item = blockIdx.x; item < a.ntiles; item += gridDim.x) {
+    const int b = rank_of_tile(item, a.tiles_per_rank);
+    const uint64_t seg = item - uint64_t(b) * a.tiles_per_rank;
+    const uint64_t base = uint64_t(b) * a.q;
+    const uint64_t cnt = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+    if (seg * kTile >= cnt) continue;
+    if ((seg + 1) * kTile <= cnt)
+      recursive_item<T, OP, P, true>(a, b, seg, cnt);
+    else
+      recursive_item<T, OP, P, false>(a, b, seg, cnt);
   }
 }
 
@@ -188,6 +280,43 @@ hipError_t run_recursive(const Call& c) {
       if (c.coll != kReduceScatter)
         for (int t = 0; t < k && e == hipSuccess; ++t) e = launch(1, t, (uint64_t(1) << t) * c.q);
       return e;
+    });
+  });
+}
+
+// Launch shape of the chained recursive driver.  Measured on float32
+// AllReduce against 1 and 2 vectors per lane and 512 lanes: four vectors
+// per lane were 1-3 % faster at N = 8 (M = 2^24, 2^26), 64 and 256, and
+// 0.5 % slower at N = 8, M = 2^28; one vector per lane was 4-7 % slower.
+#ifndef CCL_SIM_RECURSIVE_CHAIN_POLICY
+#define CCL_SIM_RECURSIVE_CHAIN_POLICY 256, 4, true, kStoreWriteThrough
+#endif
+using RecursiveChainPolicy = Policy<CCL_SIM_RECURSIVE_CHAIN_POLICY>;
+
+template <class T, int OP, class P>
+hipError_t launch_recursive_chained(const Call& c) {
+  RecArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.coll = c.coll;
+  a.q = c.q;
+  a.limit = c.limit;
+  a.scratch = c.partial;
+  a.placed = (c.coll == kAllGather && c.in_place) ? 1 : 0;
+  a.tiles_per_rank = ceil_div(c.q, tile_elems<T, P>());
+  a.ntiles = uint64_t(c.nranks) * a.tiles_per_rank;
+  if (a.ntiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((recursive_chained_kernel<T, OP, P>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(P::TB), 0,
+                     c.stream, a);
+  return hipGetLastError();
+}
+
+hipError_t run_recursive_chained(const Call& c) {
+  return by_type(c.dtype, [&]<class T>() -> hipError_t {
+    const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
+    return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
+      return launch_recursive_chained<U, OP, RecursiveChainPolicy>(c);
     });
   });
 }

@@ -13,8 +13,9 @@ dispatch) and scales each counter by what it reads for the plain copy in
 the same pass (``ccl_sim_pad_identity`` with nothing to pad, which reads
 and writes a known N·M·s bytes).  For each call of the pass it sums the
 counters over the call's dispatches of its kernel (one for the direct
-kernels and the persistent ring, 2(N-1) for the stepwise ring, 2·log2 N for
-the recursive schedule) and sets the HBM bytes beside the call's
+kernels, the persistent and chained ring and the chained recursive driver,
+2(N-1) for the stepwise ring, 2·log2 N for the stepwise recursive one) and
+sets the HBM bytes beside the call's
 algorithmic bytes.  It writes ``profiles/traffic.json`` and a Markdown
 table of the same figures.  The record carries the digest of the kernel
 sources the counters were taken on; bench.py reports the traffic only
@@ -30,7 +31,8 @@ import sys
 
 def _short(name):
     for key in ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
-                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "pad_kernel", "reset_ctrl_kernel",
+                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "recursive_chained_kernel",
+                "pad_kernel", "reset_ctrl_kernel",
                 "store_table_kernel"):
         if key in name:
             return key
@@ -157,7 +159,8 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
             "ring_step_kernel": "AllReduce, stepwise ring (all steps)",
             "ring_persistent_kernel": "AllReduce, persistent ring (one launch)",
             "ring_chained_kernel": "AllReduce, chained ring (one launch)",
-            "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)"}
+            "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)",
+            "recursive_chained_kernel": "AllReduce, chained recursive halving + doubling (one launch)"}
     lines = [
         f"# HBM traffic of the library's kernels (rocprofv3 counters), {workload}",
         "",

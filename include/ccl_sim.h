@@ -142,7 +142,15 @@ typedef enum {
    * ring schedules, bit-identical results.  The partials live in a buffer
    * keyed by chunk (N·q accumulators), since chunks no longer move in step
    * lockstep. */
-  CCL_SIM_RING_CHAINED = 4
+  CCL_SIM_RING_CHAINED = 4,
+  /* The recursive halving / doubling of CCL_SIM_RECURSIVE in one launch.
+   * Each position is reduced by its own butterfly over the ranks and
+   * gathered by its own doubling tree, so one workgroup carries a slice of
+   * block b through every halving and doubling step (all the ranks of a
+   * step in turn), with no barrier and no relaunch.  Same pairs, combining
+   * order and algorithmic bytes as CCL_SIM_RECURSIVE, bit-identical
+   * results; nranks must be a power of two (else CCL_SIM_UNSUPPORTED). */
+  CCL_SIM_RECURSIVE_CHAINED = 5
 } ccl_sim_schedule_t;
 
 typedef enum {
@@ -229,7 +237,7 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
  *     for bf16, else the element size) for ring ReduceScatter and ring
  *     AllReduce with N >= 3; N·q·a, one partial per chunk, for the chained
  *     ring;
- *   - the recursive schedule's per-rank halves N·(N/2)·q·a for its
+ *   - the recursive schedules' per-rank halves N·(N/2)·q·a for their
  *     ReduceScatter and AllReduce with N >= 4.
  * AllGather needs no partials under any schedule.
  */
@@ -241,10 +249,11 @@ size_t ccl_sim_workspace_size(ccl_sim_coll_t coll, int nranks, size_t count, ccl
  * movement must read or write, counted once per access (the numerator of
  * the effective bandwidth).  s = element size, a = accumulator size:
  *   DIRECT  ReduceScatter (N+1)·M·s    AllGather (N+1)·M·s    AllReduce 2N·M·s
- *   RECURSIVE  halving step j: each position is reduced by N/2^j ranks,
- *           each reading two partials (the inputs at step 1) and writing one
- *           (the output at the last step): 3(N-1)·M·s for 4- and 8-byte
- *           types; AllGather and the AllReduce's gather phase as the ring.
+ *   RECURSIVE (either driver)  halving step j: each position is reduced
+ *           by N/2^j ranks, each reading two partials (the inputs at step
+ *           1) and writing one (the output at the last step): 3(N-1)·M·s
+ *           for 4- and 8-byte types; AllGather and the AllReduce's gather
+ *           phase as the ring.
  *   ring    ReduceScatter: per step, each of the M positions reads the
  *           incoming partial and the rank's own element and writes the new
  *           partial; the first step's incoming partial and the last step's
@@ -261,7 +270,9 @@ uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count
 /* Compute-kernel launches one call enqueues for count > 0: DIRECT 1;
  * stepwise ring N-1 (ReduceScatter), N-1 plus 1 own-shard placement
  * (out-of-place AllGather), 2(N-1) (AllReduce) — the nsteps of [DECOMP]
- * §源码二; persistent and chained ring 1.  Not counted: the pointer-table uploads when
+ * §源码二; RECURSIVE log2 N per phase (plus the placement of an
+ * out-of-place AllGather); persistent ring, chained ring and chained
+ * recursive 1.  Not counted: the pointer-table uploads when
  * nranks > 64 and the persistent ring's barrier reset.  N = 1: 1.
  * Returns -1 for invalid arguments. */
 int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_schedule_t schedule,

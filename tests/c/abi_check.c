@@ -45,6 +45,7 @@ int main(void) {
   CHECK(ccl_sim_launch_count(CCL_SIM_COLL_ALLREDUCE, 256, 1000, CCL_SIM_RING_PERSISTENT, 0) == 1);
   CHECK(ccl_sim_launch_count(CCL_SIM_COLL_ALLREDUCE, 256, 1000, CCL_SIM_RING_CHAINED, 0) == 1);
   CHECK(ccl_sim_launch_count(CCL_SIM_COLL_ALLREDUCE, 256, 1000, CCL_SIM_RECURSIVE, 0) == 16);
+  CHECK(ccl_sim_launch_count(CCL_SIM_COLL_ALLREDUCE, 256, 1000, CCL_SIM_RECURSIVE_CHAINED, 0) == 1);
 
   /* ring routing of [RING] §2 at N = 4: step 0, rank 0 sends chunk 0 and receives chunk 3 */
   int send_chunk = -1, recv_chunk = -1;

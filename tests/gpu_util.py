@@ -9,7 +9,12 @@ from collective_reduction_amd import inputs as I
 
 TORCH = {"int32": torch.int32, "int64": torch.int64, "float32": torch.float32, "bfloat16": torch.bfloat16}
 NP = {"int32": np.int32, "int64": np.int64, "float32": np.float32, "bfloat16": np.uint16}
-SCHEDULES = ("direct", "ring_stepwise", "ring_persistent", "recursive", "ring_chained")
+SCHEDULES = ("direct", "ring_stepwise", "ring_persistent", "recursive", "ring_chained", "recursive_chained")
+
+
+def is_recursive(schedule):
+    """Both drivers of recursive halving / doubling (power-of-two N only)."""
+    return schedule.startswith("recursive")
 
 
 def pow2(n):

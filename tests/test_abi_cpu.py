@@ -68,7 +68,7 @@ def test_argument_validation(cs):
     assert code_of(ar, s, r, m, dtype="float32", op=9) == cs.INVALID_ARGUMENT
     assert code_of(ar, s, r, m, dtype="float32", op=5) == cs.INVALID_ARGUMENT
     assert code_of(ar, s, r, m, dtype=7) == cs.INVALID_ARGUMENT
-    assert code_of(ar, s, r, m, dtype="float32", schedule=5) == cs.INVALID_ARGUMENT
+    assert code_of(ar, s, r, m, dtype="float32", schedule=6) == cs.INVALID_ARGUMENT
     assert code_of(ar, [], [], m, dtype="float32") == cs.INVALID_ARGUMENT
     big = fake(1025, 1, 4)
     assert code_of(ar, big, fake(1025, 1, 4, base=BASE * 9), 1, dtype="float32") == cs.INVALID_ARGUMENT
@@ -244,6 +244,16 @@ def test_recursive_planning(cs):
     assert lc("allreduce", 6, 100, "recursive") == -1
     s, r = fake(6, 60, 4), fake(6, 60, 4, base=BASE * 3)
     assert code_of(cs.ccl_sim_allreduce, s, r, 60, dtype="float32", schedule="recursive") == cs.UNSUPPORTED
+    # the chained driver: same workspace and bytes, one launch, same power-of-two rule
+    for coll in ("reduce_scatter", "all_gather", "allreduce"):
+        for nn, mm, dt in ((8, m, "float32"), (256, 1 << 22, "bfloat16"), (2, 1000, "int64"), (4, 1003, "int32")):
+            assert ws(coll, nn, mm, dt, "recursive_chained") == ws(coll, nn, mm, dt, "recursive")
+            assert ab(coll, nn, mm, dt, "recursive_chained") == ab(coll, nn, mm, dt, "recursive")
+            assert lc(coll, nn, mm, "recursive_chained") == 1
+        assert lc(coll, 6, 100, "recursive_chained") == -1
+    assert lc("allreduce", 1, 100, "recursive_chained") == 1
+    assert code_of(cs.ccl_sim_allreduce, s, r, 60, dtype="float32", schedule="recursive_chained") == cs.UNSUPPORTED
+    assert code_of(cs.ccl_sim_allreduce, s, r, 60, dtype="float32", schedule=6) == cs.INVALID_ARGUMENT
 
 
 def test_result_strings(cs):

@@ -27,7 +27,7 @@ def cs():
 @pytest.mark.parametrize("schedule", U.SCHEDULES)
 @pytest.mark.parametrize("n,m", [(8, 3 * 8 * 1024 + 5), (100, 100 * 37 - 11)])
 def test_allreduce_graph_replays_match_eager(cs, schedule, n, m):
-    if schedule == "recursive" and not U.pow2(n):
+    if U.is_recursive(schedule) and not U.pow2(n):
         pytest.skip("recursive halving needs a power-of-two N")
     if schedule == "ring_persistent":
         pytest.skip("the persistent ring is a cooperative launch, which HIP does not document as capturable")

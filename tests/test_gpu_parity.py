@@ -35,7 +35,7 @@ def cs():
 def oracle_rs(xs, op, dtype, q, schedule):
     if schedule == "direct":
         return C.reduce_scatter(xs, op, dtype, q)
-    if schedule == "recursive":
+    if U.is_recursive(schedule):
         return H.reduce_scatter(xs, op, dtype, q)
     return G.ring_reduce_scatter(xs, op, dtype, q)
 
@@ -43,14 +43,14 @@ def oracle_rs(xs, op, dtype, q, schedule):
 def oracle_ar(xs, op, dtype, schedule):
     if schedule == "direct":
         return C.direct_allreduce(xs, op, dtype)
-    if schedule == "recursive":
+    if U.is_recursive(schedule):
         return H.allreduce(xs, op, dtype)
     return G.ring_allreduce(xs, op, dtype)
 
 
 def runs(schedule, n):
-    """The recursive schedule takes power-of-two rank counts only."""
-    return schedule != "recursive" or U.pow2(n)
+    """The recursive schedules take power-of-two rank counts only."""
+    return not U.is_recursive(schedule) or U.pow2(n)
 
 
 def assert_all_same(outs, want, what):
@@ -183,10 +183,11 @@ def test_signed_zero_ties_follow_the_combining_order(cs, dtype, op, schedule):
         assert not U.same_bits(oracle_ar(xs, op, dtype, schedule)[0], direct)
 
 
-def test_recursive_needs_a_power_of_two(cs):
+@pytest.mark.parametrize("schedule", ["recursive", "recursive_chained"])
+def test_recursive_needs_a_power_of_two(cs, schedule):
     xs = U.random_inputs(6, 60, "float32", seed=1)
     with pytest.raises(cs.CclSimError, match="power-of-two"):
-        U.run_ar(cs, xs, "sum", "float32", "recursive")
+        U.run_ar(cs, xs, "sum", "float32", schedule)
 
 
 @pytest.mark.parametrize("schedule", U.SCHEDULES)
@@ -440,7 +441,7 @@ def _sampled_check(cs, s, schedule, op, k, seed, coll="allreduce"):
     want = np.empty(pos.size, dtype=U.NP[dtype])
     if schedule == "direct":
         want[:] = R.narrow(C.fold(xs, op, dtype, list(range(n))), dtype)
-    elif schedule == "recursive":
+    elif U.is_recursive(schedule):
         # the butterfly tree is the same for every position
         want[:] = H.allreduce(xs, op, dtype)[0]
     else:
@@ -471,7 +472,7 @@ def test_gradient_256x6553600_bf16_sampled(cs, schedule):
     _sampled_check(cs, I.spec("normal_256x6553600_bf16"), schedule, "sum", 4096, 12)
 
 
-@pytest.mark.parametrize("schedule", ["direct", "ring_stepwise", "recursive"])
+@pytest.mark.parametrize("schedule", ["direct", "ring_stepwise", "recursive", "recursive_chained"])
 def test_uniform_8x256m_fp32_rs_ag_sampled(cs, schedule):
     """N=8, M=2^28 (1 GiB per rank) float32: RS then AG at full size."""
     from collective_reduction_amd import inputs as I
@@ -512,7 +513,7 @@ def test_uniform_8x256m_fp32_every_element(cs, schedule):
         cols = [x[r * q:(r + 1) * q] for x in xs]
         if schedule == "direct":
             want = R.narrow(C.fold(cols, "sum", "float32", list(range(n))), "float32")
-        elif schedule == "recursive":
+        elif U.is_recursive(schedule):
             want = H.allreduce(cols, "sum", "float32")[0]
         else:
             want = R.narrow(C.fold(cols, "sum", "float32", G.chunk_order(n, r)), "float32")

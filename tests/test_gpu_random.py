@@ -34,7 +34,7 @@ def cs():
 
 def draw(rng):
     n = int(rng.choice(RANKS))
-    schedules = [s for s in U.SCHEDULES if s != "recursive" or U.pow2(n)]
+    schedules = [s for s in U.SCHEDULES if not U.is_recursive(s) or U.pow2(n)]
     case = {
         "n": n,
         "dtype": str(rng.choice(DTYPES)),
@@ -60,7 +60,7 @@ def draw(rng):
 def oracle_rs(xs, op, dtype, q, schedule):
     if schedule == "direct":
         return C.reduce_scatter(xs, op, dtype, q)
-    if schedule == "recursive":
+    if U.is_recursive(schedule):
         return H.reduce_scatter(xs, op, dtype, q)
     return G.ring_reduce_scatter(xs, op, dtype, q)
 
@@ -68,7 +68,7 @@ def oracle_rs(xs, op, dtype, q, schedule):
 def oracle_ar(xs, op, dtype, schedule):
     if schedule == "direct":
         return C.direct_allreduce(xs, op, dtype)
-    if schedule == "recursive":
+    if U.is_recursive(schedule):
         return H.allreduce(xs, op, dtype)
     return G.ring_allreduce(xs, op, dtype)
 
