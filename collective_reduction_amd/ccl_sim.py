@@ -157,31 +157,27 @@ def _dtype_code(dtype):
     return _enum(DTYPES, dtype, "dtype")
 
 
-def _ptr(x):
-    if isinstance(x, torch.Tensor):
-        return x.data_ptr()
-    return int(x)
-
-
-def _ptr_array(bufs):
-    arr = (ctypes.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
-    return ctypes.cast(arr, _vpp), arr
-
-
 _HAVE_GPU = None
+# torch's accessor of the current stream's raw handle; it skips building a
+# Stream object, which costs more than the rest of a small call
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _stream(stream):
+def _stream(stream, dev=None):
     global _HAVE_GPU
     if stream is None:
         if _HAVE_GPU is None:
             _HAVE_GPU = torch.cuda.is_available()
-        # without a GPU the library rejects or fails the call itself; the
-        # null stream keeps argument validation reachable on a host
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream if _HAVE_GPU else 0)
+        if not _HAVE_GPU:
+            # without a GPU the library rejects or fails the call itself; the
+            # null stream keeps argument validation reachable on a host
+            return None
+        if _RAW_STREAM is not None:
+            return _RAW_STREAM(torch.cuda.current_device() if dev is None else dev)
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+        return stream.cuda_stream
+    return int(stream)
 
 
 def _infer_dtype(bufs, dtype):
@@ -209,26 +205,30 @@ def _refuse(b, r, need, code, what, dev):
     raise ValueError(f"{what}[{r}] holds {b.numel()} elements; the call needs {need}")
 
 
-def _check_tensors(bufs, need, code, what, dev=None):
-    """Rank buffers given as tensors must be contiguous device tensors of
-    the call's dtype, on the current device, holding at least `need`
-    elements: the library sees only addresses, and a host address or a
-    short buffer would reach the kernels.  Raw addresses are the caller's
-    responsibility.  Returns the current device once it has been read, so a
-    call reads it at most once (the checks run on every call, so they keep
-    to a few cheap tensor attributes)."""
+def _marshal(bufs, need, code, what, dev=None):
+    """The host array of device addresses the C ABI takes, one per rank.
+    Rank buffers given as tensors must be contiguous device tensors of the
+    call's dtype, on the current device, holding at least `need` elements:
+    the library sees only addresses, and a host address or a short buffer
+    would reach the kernels.  Raw addresses are the caller's
+    responsibility.  Also returns the current device once it has been read,
+    so a call reads it at most once (the checks run on every call, so they
+    keep to a few cheap tensor attributes)."""
     want = _CODE_TORCH.get(code)
+    ptrs = [0] * len(bufs)
     for r, b in enumerate(bufs):
-        if not isinstance(b, torch.Tensor):
-            continue
-        d = b.get_device()
-        if d < 0:
-            _refuse(b, r, need, code, what, dev)
-        if dev is None:
-            dev = torch.cuda.current_device()
-        if d != dev or b.dtype is not want or b.numel() < need or not b.is_contiguous():
-            _refuse(b, r, need, code, what, dev)
-    return dev
+        if isinstance(b, torch.Tensor):
+            d = b.get_device()
+            if d < 0:
+                _refuse(b, r, need, code, what, dev)
+            if dev is None:
+                dev = torch.cuda.current_device()
+            if d != dev or b.dtype is not want or b.numel() < need or not b.is_contiguous():
+                _refuse(b, r, need, code, what, dev)
+            ptrs[r] = b.data_ptr()
+        else:
+            ptrs[r] = int(b)
+    return (ctypes.c_void_p * len(ptrs))(*ptrs), dev
 
 
 def _ws(workspace):
@@ -253,12 +253,11 @@ def ccl_sim_reduce_scatter(sendbufs, recvbufs, sendcount, recvcount, op="sum", s
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(recvbufs, recvcount, code, "recvbufs", _check_tensors(sendbufs, sendcount, code, "sendbufs"))
-    s, _ks = _ptr_array(sendbufs)
-    r, _kr = _ptr_array(recvbufs)
+    s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
+    r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
     wp, wb = _ws(workspace)
     _check(_reduce_scatter(s, r, n, sendcount, recvcount, code, _enum(OPS, op, "op"),
-                           _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream)))
+                           _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream, dev)))
 
 
 def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direct", workspace=None, stream=None,
@@ -268,12 +267,11 @@ def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direc
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(recvbufs, recvcount, code, "recvbufs", _check_tensors(sendbufs, sendcount, code, "sendbufs"))
-    s, _ks = _ptr_array(sendbufs)
-    r, _kr = _ptr_array(recvbufs)
+    s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
+    r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
     wp, wb = _ws(workspace)
     _check(_all_gather(s, r, n, sendcount, recvcount, code, _enum(SCHEDULES, schedule, "schedule"), wp, wb,
-                       _stream(stream)))
+                       _stream(stream, dev)))
 
 
 def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", workspace=None, stream=None,
@@ -283,12 +281,11 @@ def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", wo
     if len(recvbufs) != n:
         raise ValueError("sendbufs and recvbufs must list the same ranks")
     code = _infer_dtype(sendbufs, dtype)
-    _check_tensors(recvbufs, count, code, "recvbufs", _check_tensors(sendbufs, count, code, "sendbufs"))
-    s, _ks = _ptr_array(sendbufs)
-    r, _kr = _ptr_array(recvbufs)
+    s, dev = _marshal(sendbufs, count, code, "sendbufs")
+    r, dev = _marshal(recvbufs, count, code, "recvbufs", dev)
     wp, wb = _ws(workspace)
     _check(_allreduce(s, r, n, count, code, _enum(OPS, op, "op"), _enum(SCHEDULES, schedule, "schedule"), wp, wb,
-                      _stream(stream)))
+                      _stream(stream, dev)))
 
 
 def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype=None):
@@ -297,10 +294,9 @@ def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype
     if len(srcs) != n:
         raise ValueError("srcs and dsts must list the same ranks")
     code = _infer_dtype(dsts, dtype)
-    _check_tensors(dsts, padded_count, code, "dsts", _check_tensors(srcs, count, code, "srcs"))
-    s, _ks = _ptr_array(srcs)
-    d, _kd = _ptr_array(dsts)
-    _check(_pad_identity(s, d, n, count, padded_count, code, _enum(OPS, op, "op"), _stream(stream)))
+    s, dev = _marshal(srcs, count, code, "srcs")
+    d, dev = _marshal(dsts, padded_count, code, "dsts", dev)
+    _check(_pad_identity(s, d, n, count, padded_count, code, _enum(OPS, op, "op"), _stream(stream, dev)))
 
 
 def ccl_sim_workspace_size(coll, nranks, count, dtype, schedule):
