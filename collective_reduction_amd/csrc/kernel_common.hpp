@@ -5,9 +5,11 @@
 // translation unit instantiates only what it uses.
 //
 // The kernels, for gfx950: fused N-way reduce (ReduceScatter), broadcast-copy
-// (AllGather), fused AllReduce, ring steps (one launch per step, or one
-// persistent cooperative kernel with a grid barrier), recursive halving and
-// doubling steps, identity padding.
+// (AllGather), fused AllReduce, ring steps (one launch per step, one
+// persistent cooperative kernel with a grid barrier, or one launch in which
+// each workgroup chains one chunk slice's steps), recursive halving and
+// doubling (one launch per step, or one launch in which each workgroup
+// walks one block slice's trees), identity padding.
 //
 // Pages cited:
 //   [DECOMP]  "NCCL 专家课程 07：AllReduce 等价分解、显存生命周期与 Kernel 证据"
@@ -16,8 +18,8 @@
 //   [WHY-EQ]  "为什么说 AllReduce = ReduceScatter + AllGather？——结合 NCCL Ring AllReduce"
 //   [RS-PAGE] "ReduceScatter" (集合通信)
 //
-// Work decomposition.  Every kernel is a grid-stride loop over tiles of
-// TB·V·U elements (V = 16 / sizeof(element): one 128-bit access per lane
+// Work decomposition.  Every kernel is a grid-stride loop over tiles (the
+// chained drivers: over work items of one tile each) of TB·V·U elements (V = 16 / sizeof(element): one 128-bit access per lane
 // per vector, U vectors per lane, TB lanes; TB and U are part of each
 // kernel's Policy).  A tile never crosses a shard (or ring chunk)
 // boundary, so the shard a tile belongs to is one scalar division per tile
@@ -68,7 +70,10 @@ enum StoreMode : int {
                            // accumulators of bf16 data, two 128-bit halves
                            // per lane): as kStoreNontemporal, since a
                            // write-through half covers only every other
-                           // 16 bytes of a line and measured slower
+                           // 16 bytes of a line and measured slower, except
+                           // for partials a kernel reads back with its own
+                           // tiling, which Lane::store_part lays out so
+                           // that they can write through
 };
 template <int TB_, int U_, bool NTL_, int ST_>
 struct Policy {
