@@ -11,8 +11,9 @@ the schedule's algorithmic bytes 2(N+1)·M·4 divided by the time per step.
 
 Also reported: per-kernel durations from HIP events on the launch stream
 (the roofline of the dominant kernel); on the same buffers, the other
-schedules (ring stepwise / persistent and recursive RS+AG, every
-schedule's AllReduce, RS alone, smaller M), timed in interleaved rounds;
+schedules (RS+AG under the three ring drivers and both recursive drivers,
+every schedule's AllReduce, RS alone, smaller M), timed in interleaved
+rounds;
 the 256-rank float32 and bf16 workloads; the alpha-beta model of the same
 payload on two networks; the measured buffer lifetimes; and the CPU oracle
 timed on a bounded sample of the workload.  Prints exactly one JSON line on
