@@ -441,7 +441,7 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
         sv = [t[:mm] for t in send]
         rv = [t[:mm] for t in recv]
         hv = [t[:qq] for t in shards]
-        for sched in ("direct", "ring_stepwise"):
+        for sched in ("direct", "ring_stepwise", "ring_chained", "recursive_chained"):
             cases.append((f"rs_ag_{sched}_m2^{lg}", lambda s=sched, sv=sv, rv=rv, hv=hv, mm=mm, qq=qq: (
                 cs.ccl_sim_reduce_scatter(sv, hv, mm, qq, schedule=s, workspace=ws, stream=stream),
                 cs.ccl_sim_all_gather(hv, rv, qq, mm, schedule=s, workspace=ws, stream=stream)),
