@@ -15,8 +15,8 @@ Routing ([RING] §1 流程, the N=4 table of §2 and the pseudocode under
 * AllGather phase, steps t = 0..N-2: rank r sends chunk (r + 1 - t) and
   receives chunk (r - t), overwriting its copy (no reduction).
 
-[RS-PAGE] §Ring ReduceScatter words step 1 as "node i sends chunk (i+1)%N",
-which contradicts the ownership it states two lines later (node 0 ends with
+[RS-PAGE] §Ring ReduceScatter has node i send chunk i+1 (mod N) at step 1,
+which contradicts the ownership the same section states (node 0 ends with
 chunk 1); the routing above is the one the other four pages agree on.
 
 All sends of a step are taken before any receive of that step is applied,
