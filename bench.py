@@ -13,11 +13,11 @@ Also reported: per-kernel durations from HIP events on the launch stream
 (the roofline of the dominant kernel); on the same buffers, the other
 schedules (RS+AG under the three ring drivers and both recursive drivers,
 every schedule's AllReduce, RS alone, smaller M), timed in interleaved
-rounds;
-the 256-rank float32 and bf16 workloads; the alpha-beta model of the same
-payload on two networks; the measured buffer lifetimes; and the CPU oracle
-timed on a bounded sample of the workload.  Prints exactly one JSON line on
-stdout; progress goes to stderr.
+rounds; the 256-rank float32 and bf16 workloads and the bench's shape in
+bf16; the alpha-beta model of the same payload on two networks; the
+measured buffer lifetimes; and the CPU oracle timed on a bounded sample of
+the workload.  Prints exactly one JSON line on stdout; progress goes to
+stderr.
 """
 
 import argparse
@@ -264,7 +264,7 @@ def main():
         secondary = run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, args.secondary_iters)
         del send, shards, recv
         torch.cuda.empty_cache()
-        secondary.update(run_many_ranks(cs, torch, stream, args.secondary_iters))
+        secondary.update(run_more_workloads(cs, torch, stream, args.secondary_iters))
         secondary.update(run_small(cs, torch, stream))
 
     # Modeled context only (not a measurement, not a target): the pages'
@@ -459,25 +459,31 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
     return time_interleaved(torch, stream, cases, iters, context)
 
 
-def run_many_ranks(cs, torch, stream, iters):
-    """The 256-rank workloads (M=2^22 float32; the 6,553,600-element bf16
-    bucket) on freshly drawn device buffers: every schedule's AllReduce and
-    the direct RS+AG, timed together by time_interleaved."""
+def run_more_workloads(cs, torch, stream, iters):
+    """On freshly drawn device buffers, timed together per workload by
+    time_interleaved: the 256-rank workloads (M=2^22 float32 and the
+    6,553,600-element bf16 bucket, normal(0, 1e-3)) under every schedule's
+    AllReduce and the direct RS+AG; and the bench's own shape in bf16 (N=8,
+    M=2^28, uniform[-1,1)) under the direct RS+AG and the direct and chained
+    AllReduces."""
     res = {}
     ab = cs.ccl_sim_algorithmic_bytes
-    for name, m, tdt, dtype in (("256x4194304_fp32", 1 << 22, torch.float32, "float32"),
-                                ("256x6553600_bf16", 6_553_600, torch.bfloat16, "bfloat16")):
-        n = 256
+    for name, n, m, tdt, dtype, scheds in (
+            ("256x4194304_fp32", 256, 1 << 22, torch.float32, "float32", ("direct",) + RING_AND_RECURSIVE),
+            ("256x6553600_bf16", 256, 6_553_600, torch.bfloat16, "bfloat16", ("direct",) + RING_AND_RECURSIVE),
+            ("8x268435456_bf16", 8, 1 << 28, torch.bfloat16, "bfloat16", ("direct", "ring_chained", "recursive_chained"))):
         q = m // n
-        send = [torch.randn(m, device="cuda").mul_(1e-3).to(tdt) for _ in range(n)]
+        if n == 256:
+            send = [torch.randn(m, device="cuda").mul_(1e-3).to(tdt) for _ in range(n)]
+        else:
+            send = [torch.rand(m, device="cuda").mul_(2).sub_(1).to(tdt) for _ in range(n)]
         recv = [torch.empty(m, dtype=tdt, device="cuda") for _ in range(n)]
         shards = [torch.empty(q, dtype=tdt, device="cuda") for _ in range(n)]
-        ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce")
-                                   for s in ("direct",) + RING_AND_RECURSIVE])
+        ws = cs.Workspace.largest([(c, n, m, dtype, s) for c in ("reduce_scatter", "allreduce") for s in scheds])
         torch.cuda.synchronize()
         cases = [(f"allreduce_{sched}_{name}", lambda s=sched: cs.ccl_sim_allreduce(
                     send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched))
-                 for sched in ("direct",) + RING_AND_RECURSIVE]
+                 for sched in scheds]
         cases.append((f"rs_ag_direct_{name}", lambda: (
             cs.ccl_sim_reduce_scatter(send, shards, m, q, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, workspace=ws, stream=stream)),
