@@ -94,6 +94,10 @@ def trace(trace_csv, out_md, command):
         command,
         "```",
         "",
+        "The rows come from the run's per-dispatch `kernel_trace.csv`. rocprofv3's own `--stats` table averages "
+        "every launch of one kernel instance across sizes; here launches are grouped by kernel, launch shape and "
+        "grid size, so that the bench step's launches (the largest grids) keep a row of their own.",
+        "",
         "| kernel | workgroups | calls | average µs | min µs | max µs | total ms |",
         "|---|---:|---:|---:|---:|---:|---:|",
     ]
