@@ -92,6 +92,7 @@ _recursive_route = _sig("ccl_sim_recursive_route", ctypes.c_int,
                         [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)])
 _result_string = _sig("ccl_sim_result_string", ctypes.c_char_p, [ctypes.c_int])
+_persistent_aborted = _sig("ccl_sim_persistent_aborted", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)])
 _last_error = _sig("ccl_sim_last_error", ctypes.c_char_p, [])
 _version = _sig("ccl_sim_version", ctypes.c_int, [])
 
@@ -117,7 +118,8 @@ MODEL_ALGOS = {"ring": 0, "tree": 1, "2level": 2}
 EXPORTED = ("ccl_sim_reduce_scatter", "ccl_sim_all_gather", "ccl_sim_allreduce", "ccl_sim_pad_identity",
             "ccl_sim_workspace_size", "ccl_sim_algorithmic_bytes", "ccl_sim_launch_count", "ccl_sim_ring_owner",
             "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version",
-            "ccl_sim_model_estimate", "ccl_sim_busbw_factor", "ccl_sim_recursive_route")
+            "ccl_sim_model_estimate", "ccl_sim_busbw_factor", "ccl_sim_recursive_route",
+            "ccl_sim_persistent_aborted")
 
 
 class CclSimError(RuntimeError):
@@ -331,6 +333,16 @@ def ccl_sim_recursive_route(nranks, phase, step, rank):
     p, f, nb = ctypes.c_int(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(_recursive_route(nranks, phase, step, rank, ctypes.byref(p), ctypes.byref(f), ctypes.byref(nb)))
     return p.value, f.value, nb.value
+
+
+def ccl_sim_persistent_aborted(workspace):
+    """True if the last persistent-ring call that used `workspace` stopped
+    at its barrier's poll limit (its outputs are then incomplete).  Call it
+    once that call's stream work has completed."""
+    wp, _ = _ws(workspace)
+    flag = ctypes.c_int()
+    _check(_persistent_aborted(wp, ctypes.byref(flag)))
+    return bool(flag.value)
 
 
 def ccl_sim_result_string(code):

@@ -106,7 +106,7 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
 
 std::atomic<int> g_cus[64];
 
-// Environment knobs, read once.
+// Environment knobs (read on every call; see env()).
 //   CCL_SIM_DEBUG=1                      log each launch plan to stderr; after a
 //                                        persistent ring, wait for it and report a
 //                                        barrier that hit its poll limit
@@ -123,10 +123,9 @@ struct Env {
   }
 };
 
-const Env& env() {
-  static const Env e;
-  return e;
-}
+// Three getenv lookups per call, so that a process can change a knob
+// between calls.
+Env env() { return Env(); }
 
 hipError_t device_cus(int* cus) {
   int dev = 0;
@@ -291,9 +290,10 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (lay.partial != SIZE_MAX) c.partial = ws + lay.partial;
   if (lay.ctrl != SIZE_MAX) c.ctrl = reinterpret_cast<unsigned*>(ws + lay.ctrl);
   c.stream = stream;
-  c.persistent_per_cu = env().per_cu;
-  c.spin_limit = env().spin_limit;
-  c.log_plan = env().debug;
+  const Env knobs = env();
+  c.persistent_per_cu = knobs.per_cu;
+  c.spin_limit = knobs.spin_limit;
+  c.log_plan = knobs.debug;
 
   hipError_t e = device_cus(&c.num_cus);
   if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "device query failed: %s", hipGetErrorString(e));
@@ -328,7 +328,12 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     PersistentPlan plan;
     e = run_ring_persistent(c, &unsupported, &plan);
     if (e == hipSuccess && unsupported)
-      return fail(CCL_SIM_UNSUPPORTED, "no co-resident grid for the persistent ring kernel on this device");
+      return plan.refused != hipSuccess
+                 ? fail(CCL_SIM_UNSUPPORTED,
+                        "the runtime refused the persistent ring's cooperative launch (%s); another process on "
+                        "this GPU may hold the device's cooperative launch resources",
+                        hipGetErrorString(plan.refused))
+                 : fail(CCL_SIM_UNSUPPORTED, "no co-resident grid for the persistent ring kernel on this device");
     if (c.log_plan)
       std::fprintf(stderr,
                    "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu lanes=%d "
@@ -553,6 +558,19 @@ const char* ccl_sim_result_string(ccl_sim_result_t result) {
 }
 
 const char* ccl_sim_last_error(void) { return g_last_error.c_str(); }
+
+ccl_sim_result_t ccl_sim_persistent_aborted(const void* workspace, int* aborted) {
+  g_last_error.clear();
+  if (workspace == nullptr || aborted == nullptr)
+    return fail(CCL_SIM_INVALID_ARGUMENT, "workspace and aborted must not be NULL");
+  // The control block opens the persistent ring's workspace (layout()).
+  unsigned word = 0;
+  const hipError_t e = hipMemcpy(&word, static_cast<const unsigned*>(workspace) + kCtrlAbort, sizeof(word),
+                                 hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "reading the abort word failed: %s", hipGetErrorString(e));
+  *aborted = word != 0 ? 1 : 0;
+  return CCL_SIM_SUCCESS;
+}
 
 int ccl_sim_version(void) { return CCL_SIM_VERSION; }
 

@@ -413,9 +413,17 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
   void* args[] = {&a};
   e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(grid)), dim3(P::TB),
                                  args, 0, c.stream);
-  if (e == hipErrorCooperativeLaunchTooLarge) {
-    (void)hipGetLastError();
+  if (e == hipSuccess) return hipSuccess;
+  // The call reports the failure; clear HIP's last-error slot so that it
+  // does not resurface in the caller's next, unrelated HIP call.
+  (void)hipGetLastError();
+  if (e == hipErrorCooperativeLaunchTooLarge || e == hipErrorIllegalState) {
+    // Too large: no co-resident grid.  Illegal state: the runtime refused the
+    // cooperative launch itself, as it does here when another process on
+    // the GPU has made cooperative launches.  Either way the request is
+    // valid but cannot run now.
     *unsupported = true;
+    if (plan && e == hipErrorIllegalState) plan->refused = e;
     return hipSuccess;
   }
   return e;

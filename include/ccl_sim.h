@@ -124,7 +124,10 @@ typedef enum {
   /* The ring of [RING] §1 / [PRIMS] §五: one kernel launch per ring step. */
   CCL_SIM_RING_STEPWISE = 1,
   /* The same ring steps inside one cooperative kernel, a grid-wide barrier
-   * between steps. */
+   * between steps.  CCL_SIM_UNSUPPORTED when the device cannot keep the
+   * grid resident, or when the runtime refuses the cooperative launch (ROCm
+   * does, for instance, while another process on the same GPU holds its
+   * cooperative launch resources); the other schedules are unaffected. */
   CCL_SIM_RING_PERSISTENT = 2,
   /* Recursive-halving ReduceScatter and recursive-doubling AllGather
    * ([RS-PAGE] §Recursive Halving ReduceScatter): log2 N steps per phase, one
@@ -371,6 +374,28 @@ ccl_sim_result_t ccl_sim_recursive_route(int nranks, int phase, int step, int ra
                                          size_t* first_block, size_t* nblocks);
 
 const char* ccl_sim_result_string(ccl_sim_result_t result);
+
+/*
+ * The persistent ring's watchdog (a diagnostic, not an operation of the
+ * pages).  Its grid barrier polls a bounded number of times.  A barrier
+ * can run into that bound only if the device does not keep the whole
+ * cooperative grid resident (for instance while other work holds its
+ * compute units); every workgroup then stops, the call's outputs are
+ * incomplete, and the kernel raises an abort word in the workspace's
+ * control block.  The call itself returns before the kernel runs, so it
+ * cannot report this.  After the stream work of a CCL_SIM_RING_PERSISTENT
+ * call with nranks >= 2 has completed, ccl_sim_persistent_aborted(workspace,
+ * &aborted) reads that word (one synchronous device-to-host copy of 4 bytes
+ * on the null stream; the control block opens the workspace): *aborted = 1 if the last persistent call that used this
+ * workspace stopped early, 0 if it ran to the end.  CCL_SIM_INVALID_ARGUMENT
+ * for NULL pointers, CCL_SIM_HIP_ERROR if the copy fails.  Setting the
+ * environment variable CCL_SIM_DEBUG=1 makes every persistent call wait
+ * for its kernel and return CCL_SIM_HIP_ERROR itself when it aborted.
+ * CCL_SIM_SPIN_LIMIT=n sets the poll limit (default 2^22); a tiny value
+ * forces the abort from the host, for tests of this path.  Both are read
+ * on every call.
+ */
+ccl_sim_result_t ccl_sim_persistent_aborted(const void* workspace, int* aborted);
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* ccl_sim_last_error(void);

@@ -87,6 +87,10 @@ int main(void) {
   CHECK(ccl_sim_allreduce(sends, recvs, 6, 16, CCL_SIM_FLOAT32, CCL_SIM_SUM, CCL_SIM_RECURSIVE, NULL, 0, NULL) ==
         CCL_SIM_UNSUPPORTED);
   CHECK(strcmp(ccl_sim_result_string(CCL_SIM_SUCCESS), "") != 0);
+  /* the watchdog query validates its pointers before any HIP call */
+  int aborted = -1;
+  CHECK(ccl_sim_persistent_aborted(NULL, &aborted) == CCL_SIM_INVALID_ARGUMENT && aborted == -1);
+  CHECK(ccl_sim_persistent_aborted(sends[0], NULL) == CCL_SIM_INVALID_ARGUMENT);
 
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;
