@@ -26,6 +26,10 @@ using namespace ccl;
 
 thread_local std::string g_last_error;
 
+// Records the message for ccl_sim_last_error() and returns `code`.  A HIP
+// failure is reported through the returned code, so HIP's own last-error
+// slot is cleared as well: left set, it would resurface in the caller's
+// next, unrelated HIP call.
 ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -33,6 +37,7 @@ ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
   std::vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  if (code == CCL_SIM_HIP_ERROR) (void)hipGetLastError();
   return code;
 }
 
