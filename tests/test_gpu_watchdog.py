@@ -72,7 +72,7 @@ def check_recovery(cs, send, ws, n, m):
 
 
 def test_forced_abort_is_reported_and_the_next_calls_run(cs, knobs):
-    n, m = 8, 1 << 24
+    n, m = 8, 1 << 26  # 16 tiles per workgroup per step: arrivals spread far beyond two polls
     send, recv = allreduce_case(n, m)
     ws = cs.Workspace("allreduce", n, m, "float32", "ring_persistent")
     knobs["CCL_SIM_SPIN_LIMIT"] = "1"
@@ -84,7 +84,7 @@ def test_forced_abort_is_reported_and_the_next_calls_run(cs, knobs):
 
 
 def test_forced_abort_is_an_error_in_debug_mode(cs, knobs):
-    n, m = 8, 1 << 24
+    n, m = 8, 1 << 26  # 16 tiles per workgroup per step: arrivals spread far beyond two polls
     send, recv = allreduce_case(n, m)
     ws = cs.Workspace("allreduce", n, m, "float32", "ring_persistent")
     knobs["CCL_SIM_SPIN_LIMIT"] = "1"
