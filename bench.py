@@ -502,9 +502,10 @@ def run_small(cs, torch, stream, calls=100):
     events, after one warm-up, so the per-call time includes the launch
     cost: RS+AG with the direct, stepwise-ring and chained-ring schedules,
     and a 64-element direct AllReduce, which moves almost nothing and so
-    measures what one call costs in launch alone; then the direct and
-    stepwise-ring RS+AG once more, captured into a HIP graph and replayed,
-    which leaves out the host's per-call work."""
+    measures what one call costs in launch alone; the direct RS+AG and the
+    64-element AllReduce again through Plans, which marshal their arguments
+    once; then the direct and stepwise-ring RS+AG once more, captured into a
+    HIP graph and replayed, which leaves out the host's per-call work."""
     from collective_reduction_amd import inputs as I
     s = I.spec("uniform_8x1048576_fp32")
     n, m = s["nranks"], s["count"]
@@ -538,6 +539,14 @@ def run_small(cs, torch, stream, calls=100):
             ab("reduce_scatter", n, m, "float32", sched) + ab("all_gather", n, m, "float32", sched))
     tiny_in, tiny_out = [t[:64] for t in send], [t[:64] for t in recv]
     timed("launch_floor_allreduce_direct_8x64", lambda: cs.ccl_sim_allreduce(tiny_in, tiny_out, 64, stream=stream), 0)
+    # the same calls through Plans, which marshal their arguments once
+    rs_plan = cs.Plan("reduce_scatter", send, shards, m, q)
+    ag_plan = cs.Plan("all_gather", shards, recv, q, m)
+    timed("rs_ag_direct_8x1048576_fp32_cache_resident_plan", lambda: (rs_plan.run(stream), ag_plan.run(stream)),
+          ab("reduce_scatter", n, m, "float32", "direct") + ab("all_gather", n, m, "float32", "direct"))
+    tiny_plan = cs.Plan("allreduce", tiny_in, tiny_out, 64)
+    timed("launch_floor_allreduce_direct_8x64_plan", lambda: tiny_plan.run(stream), 0)
+    del rs_plan, ag_plan, tiny_plan
     # the same RS+AG steps captured once into a HIP graph and replayed: no
     # per-call host work, so what remains is the GPU's own time
     for sched in ("direct", "ring_stepwise"):

@@ -301,6 +301,57 @@ def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype
     _check(_pad_identity(s, d, n, count, padded_count, code, _enum(OPS, op, "op"), _stream(stream, dev)))
 
 
+class Plan:
+    """One collective call with its arguments marshalled once, for loops that
+    repeat the same call on the same buffers (a training step's gradient
+    buckets, a serving loop).  The binding's tensor checks and the arrays of
+    device addresses are done here, at creation; run() only issues the C
+    call, which still validates every argument before it enqueues anything.
+    The plan keeps references to its tensors and workspace, so their memory
+    stays valid; their contents may change between runs, but the tensors
+    must not be replaced or resized.
+
+        plan = Plan("allreduce", send, recv, count, op="sum", schedule="ring_chained", workspace=ws)
+        plan.run()              # on torch's current stream
+        plan.run(stream=s)      # or on a given stream
+
+    For "reduce_scatter" and "all_gather" give sendcount and recvcount as for
+    the functions of the same names; for "allreduce" and "pad_identity" the
+    counts are count (and padded_count)."""
+
+    def __init__(self, coll, sendbufs, recvbufs, sendcount, recvcount=None, op="sum", schedule="direct",
+                 workspace=None, dtype=None):
+        n = len(sendbufs)
+        if len(recvbufs) != n:
+            raise ValueError("sendbufs and recvbufs must list the same ranks")
+        self.coll = coll
+        code = _infer_dtype(recvbufs if coll == "pad_identity" else sendbufs, dtype)
+        if coll in ("allreduce",):
+            recvcount = sendcount
+        elif recvcount is None:
+            raise ValueError(f"{coll} needs both counts")
+        s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
+        r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
+        wp, wb = _ws(workspace)
+        self._dev = dev
+        self._keep = (sendbufs, recvbufs, workspace, s, r)
+        sched = _enum(SCHEDULES, schedule, "schedule")
+        if coll == "reduce_scatter":
+            self._fn, self._args = _reduce_scatter, (s, r, n, sendcount, recvcount, code, _enum(OPS, op, "op"),
+                                                     sched, wp, wb)
+        elif coll == "all_gather":
+            self._fn, self._args = _all_gather, (s, r, n, sendcount, recvcount, code, sched, wp, wb)
+        elif coll == "allreduce":
+            self._fn, self._args = _allreduce, (s, r, n, sendcount, code, _enum(OPS, op, "op"), sched, wp, wb)
+        elif coll == "pad_identity":
+            self._fn, self._args = _pad_identity, (s, r, n, sendcount, recvcount, code, _enum(OPS, op, "op"))
+        else:
+            raise ValueError(f"unknown collective {coll!r}")
+
+    def run(self, stream=None):
+        _check(self._fn(*self._args, _stream(stream, self._dev)))
+
+
 def ccl_sim_workspace_size(coll, nranks, count, dtype, schedule):
     return _workspace_size(_enum(COLLS, coll, "coll"), nranks, count, _dtype_code(dtype),
                            _enum(SCHEDULES, schedule, "schedule"))

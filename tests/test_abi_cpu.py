@@ -120,6 +120,22 @@ def test_binding_rejects_host_tensors(cs):
             call()
 
 
+def test_plan_checks_at_creation_and_validates_at_run(cs):
+    """A Plan refuses host tensors when it is made; counts are validated by
+    the library on every run, before anything is enqueued."""
+    import torch
+    with pytest.raises(ValueError, match="device buffers"):
+        cs.Plan("allreduce", [torch.zeros(8)] * 2, [torch.zeros(8)] * 2, 8)
+    with pytest.raises(ValueError, match="both counts"):
+        cs.Plan("reduce_scatter", fake(4, 100, 4), fake(4, 25, 4, base=BASE * 3), 100, dtype="float32")
+    with pytest.raises(ValueError, match="unknown collective"):
+        cs.Plan("broadcast", fake(4, 100, 4), fake(4, 100, 4, base=BASE * 3), 100, 100, dtype="float32")
+    plan = cs.Plan("reduce_scatter", fake(4, 1003, 8), fake(4, 250, 8, base=BASE * 3), 1003, 250, dtype="int64")
+    for _ in range(2):
+        with pytest.raises(TypeError, match="input tensor must be the same size"):
+            plan.run()
+
+
 def test_in_place_forms_pass_validation_overlap(cs):
     """The in-place forms are accepted by the overlap check (the call then
     fails only at the first HIP call when no GPU is present)."""

@@ -340,6 +340,35 @@ def test_binding_checks_tensor_arguments(cs):
     assert all(bool((x == float(n)).all()) for x in recv)
 
 
+@pytest.mark.parametrize("schedule", ["direct", "ring_chained", "recursive_chained"])
+def test_plan_runs_match_direct_calls(cs, schedule):
+    """A Plan marshals its arguments once; each run must give what the
+    function call gives, also after the inputs' contents change."""
+    n, q = 8, 3001
+    m = n * q
+    xs = U.random_inputs(n, m, "float32", seed=71)
+    send = U.bufs_from(xs, "float32")
+    shards = [U.empty(q, "float32") for _ in range(n)]
+    gathered = [U.empty(m, "float32") for _ in range(n)]
+    ar = [U.empty(m, "float32") for _ in range(n)]
+    ws = cs.Workspace.largest([(c, n, m, "float32", schedule) for c in ("reduce_scatter", "all_gather", "allreduce")])
+    plans = [cs.Plan("reduce_scatter", send, shards, m, q, schedule=schedule, workspace=ws),
+             cs.Plan("all_gather", shards, gathered, q, m, schedule=schedule, workspace=ws),
+             cs.Plan("allreduce", send, ar, m, op="max", schedule=schedule, workspace=ws)]
+    for round_ in range(2):
+        for p in plans:
+            p.run()
+        torch.cuda.synchronize()
+        want_rs = oracle_rs(xs, "sum", "float32", q, schedule)
+        for r in range(n):
+            assert U.same_bits(U.to_host(shards[r], "float32"), want_rs[r]), (round_, r)
+        assert_all_same([U.to_host(g, "float32") for g in gathered], C.all_gather(want_rs, m)[0], "plan AG")
+        assert_all_same([U.to_host(a, "float32") for a in ar], oracle_ar(xs, "max", "float32", schedule)[0], "plan AR")
+        xs = U.random_inputs(n, m, "float32", seed=72 + round_)
+        for t, x in zip(send, xs):
+            t.copy_(U.to_dev(x, "float32"))
+
+
 def test_pad_in_place_fills_only_the_tail(cs):
     n, m, p = 3, 1000, 1024
     xs = U.random_inputs(n, p, "float32", seed=3)
