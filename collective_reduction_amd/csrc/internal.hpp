@@ -40,6 +40,7 @@ struct PersistentPlan {
   uint64_t tiles_per_step = 0;
   int lanes = 0;  // threads per workgroup
   hipError_t refused = hipSuccess;  // the cooperative launch's error when the runtime refused it
+  bool coherent = false;            // agent-coherent data path, barrier without cache maintenance
 };
 
 // Control block of the persistent ring (unsigned words): line 0 holds the

@@ -182,6 +182,73 @@ __device__ inline void store_through(void* tile_base, uint32_t tile_bytes, uint3
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(W4, v), rs, int(byte_offset), 0, kSystemScope);
 }
 
+// Agent-coherent accesses, for data that other workgroups, on any of the
+// eight XCDs, wrote earlier in the same kernel (the persistent ring's
+// partials and forwarded chunks).  Each XCD has its own L2, and a plain load
+// may hit a line that another XCD has since rewritten.  A load with sc1
+// (agent scope) is coherent across the device, and a store with sc0 sc1
+// writes through to memory; once a wave's such stores have completed
+// (vmcnt 0), any later agent-scope load on the device sees them.  A grid
+// barrier between such accesses then needs no cache write-back or
+// invalidation, only the arrival counters.  The accesses go through a
+// buffer resource over the workgroup's tile (only buffer instructions take
+// explicit cache bits); element accesses cover the ragged ends.
+constexpr int kAgentScope = 16;  // sc1
+using W4 = unsigned __attribute__((ext_vector_type(4)));
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* tile_base, uint32_t tile_bytes) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(tile_base);
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(addr))));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32))));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), 0, int(tile_bytes), kRsrcWord3);
+}
+template <class EV>
+__device__ inline EV load_vec_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(EV) == 16) {
+    return __builtin_bit_cast(EV, __builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, kAgentScope));
+  } else {
+    static_assert(sizeof(EV) == 32, "one or two 128-bit vectors");
+    struct Pair {
+      W4 lo, hi;
+    };
+    const Pair p{__builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, kAgentScope),
+                 __builtin_amdgcn_raw_buffer_load_b128(rs, int(off) + 16, 0, kAgentScope)};
+    return __builtin_bit_cast(EV, p);
+  }
+}
+template <class EV>
+__device__ inline void store_vec_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off, EV v) {
+  if constexpr (sizeof(EV) == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(W4, v), rs, int(off), 0, kSystemScope);
+  } else {
+    static_assert(sizeof(EV) == 32, "one or two 128-bit vectors");
+    struct Pair {
+      W4 lo, hi;
+    };
+    const Pair p = __builtin_bit_cast(Pair, v);
+    __builtin_amdgcn_raw_buffer_store_b128(p.lo, rs, int(off), 0, kSystemScope);
+    __builtin_amdgcn_raw_buffer_store_b128(p.hi, rs, int(off) + 16, 0, kSystemScope);
+  }
+}
+template <class E>
+__device__ inline E load1_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  if constexpr (sizeof(E) == 2)
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(rs, int(off), 0, kAgentScope));
+  else if constexpr (sizeof(E) == 4)
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, int(off), 0, kAgentScope));
+  else
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, int(off), 0, kAgentScope));
+}
+template <class E>
+__device__ inline void store1_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off, E v) {
+  if constexpr (sizeof(E) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs, int(off), 0, kSystemScope);
+  else if constexpr (sizeof(E) == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), rs, int(off), 0, kSystemScope);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(unsigned __attribute__((ext_vector_type(2))), v), rs,
+                                          int(off), 0, kSystemScope);
+}
+
 __device__ inline int rank_of_tile(uint64_t tile, uint64_t per) { return static_cast<int>(tile / per); }
 
 __device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
@@ -192,7 +259,7 @@ __device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
 // the valid range, so every vector is complete and no lane checks a count;
 // otherwise each vector carries its count of valid elements (0..V) and
 // incomplete ones move element by element.
-template <class T, class P, bool FULL>
+template <class T, class P, bool FULL, bool CO = false>
 struct Lane {
   using S = typename T::S;
   using A = typename T::A;
@@ -217,8 +284,30 @@ struct Lane {
   __device__ bool on(int u) const { return FULL || cnt[u] > 0; }
   __device__ bool whole(int u) const { return FULL || cnt[u] == V; }
 
+  // CO: every access agent-coherent (see load_vec_coherent).  The
+  // resource spans the full tile from t0; a lane's vector u starts at
+  // element (u·TB + lane)·V of it.
+  template <class E>
+  __device__ __amdgpu_buffer_rsrc_t rsrc(const E* base) const {
+    return tile_rsrc(base + t0, uint32_t(tile_of<P>(V) * sizeof(E)));
+  }
+  template <class E>
+  __device__ uint32_t offset(int u) const {
+    return uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * V * int(sizeof(E)));
+  }
+
   template <class E, class EV>
   __device__ EV load_any(const E* base, int u) const {
+    if constexpr (CO) {
+      const auto rs = rsrc(base);
+      const uint32_t off = offset<E>(u);
+      if (whole(u)) return load_vec_coherent<EV>(rs, off);
+      EV v = {};
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+        if (k < cnt[u]) v[k] = load1_coherent<E>(rs, off + uint32_t(k * int(sizeof(E))));
+      return v;
+    }
     if (whole(u)) return vload<E, V, P::NTL>(base + j[u]);
     EV v = {};
 #pragma unroll
@@ -228,6 +317,19 @@ struct Lane {
   }
   template <class E, class EV>
   __device__ void store_any(E* base, int u, EV v) const {
+    if constexpr (CO) {
+      static_assert(P::ST == kStoreWriteThrough, "coherent stores write through");
+      const auto rs = rsrc(base);
+      const uint32_t off = offset<E>(u);
+      if (whole(u)) {
+        store_vec_coherent<EV>(rs, off, v);
+        return;
+      }
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+        if (k < cnt[u]) store1_coherent<E>(rs, off + uint32_t(k * int(sizeof(E))), static_cast<E>(v[k]));
+      return;
+    }
     if (whole(u)) {
       // a whole vector, also in the last, ragged tile of a shard: the
       // resource spans the full tile, but only valid vectors are stored
@@ -264,9 +366,17 @@ struct Lane {
     if constexpr (kSplitAcc) {
       if (split()) {
         using H = typename VecOf<A, V / 2>::type;
-        const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
-        const H lo = vload<A, V / 2, P::NTL>(half0);
-        const H hi = vload<A, V / 2, P::NTL>(half0 + tv / 2);
+        H lo, hi;
+        if constexpr (CO) {
+          const auto rs = tile_rsrc(base + t0, uint32_t(tv * sizeof(A)));
+          const uint32_t off = uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(H)));
+          lo = load_vec_coherent<H>(rs, off);
+          hi = load_vec_coherent<H>(rs, off + uint32_t(tv / 2 * sizeof(A)));
+        } else {
+          const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
+          lo = vload<A, V / 2, P::NTL>(half0);
+          hi = vload<A, V / 2, P::NTL>(half0 + tv / 2);
+        }
         AV v;
 #pragma unroll
         for (int k = 0; k < V / 2; ++k) {
@@ -358,9 +468,9 @@ __device__ inline SV finish_vec(const typename T::A (&acc)[vec_elems<T>()], int 
 
 // Copy of `len` elements from src to dst for one tile (AllGather steps and
 // the stand-alone AllGather's own-shard placement).
-template <class T, class P, bool FULL>
+template <class T, class P, bool FULL, bool CO = false>
 __device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, uint64_t seg, uint64_t len) {
-  using L = Lane<T, P, FULL>;
+  using L = Lane<T, P, FULL, CO>;
   const L ln(seg, len);
   typename L::SV v[P::U];
 #pragma unroll
