@@ -389,7 +389,9 @@ def ccl_sim_recursive_route(nranks, phase, step, rank):
 def ccl_sim_persistent_aborted(workspace):
     """True if the last persistent-ring call that used `workspace` stopped
     at its barrier's poll limit (its outputs are then incomplete).  Call it
-    once that call's stream work has completed."""
+    once that call's stream work has completed, and before another call
+    reuses the workspace (the other schedules keep their partials where the
+    persistent ring's control block was)."""
     wp, _ = _ws(workspace)
     flag = ctypes.c_int()
     _check(_persistent_aborted(wp, ctypes.byref(flag)))

@@ -386,11 +386,14 @@ const char* ccl_sim_result_string(ccl_sim_result_t result);
  * cannot report this.  After the stream work of a CCL_SIM_RING_PERSISTENT
  * call with nranks >= 2 has completed, ccl_sim_persistent_aborted(workspace,
  * &aborted) reads that word (one synchronous device-to-host copy of 4 bytes
- * on the null stream; the control block opens the workspace): *aborted = 1 if the last persistent call that used this
- * workspace stopped early, 0 if it ran to the end.  CCL_SIM_INVALID_ARGUMENT
- * for NULL pointers, CCL_SIM_HIP_ERROR if the copy fails.  Setting the
- * environment variable CCL_SIM_DEBUG=1 makes every persistent call wait
- * for its kernel and return CCL_SIM_HIP_ERROR itself when it aborted.
+ * on the null stream; the control block opens the workspace): *aborted = 1
+ * if the last persistent call that used this workspace stopped early, 0 if
+ * it ran to the end.  Query before another call reuses the workspace: the
+ * other schedules keep their partials where the control block was.
+ * CCL_SIM_INVALID_ARGUMENT for NULL pointers, CCL_SIM_HIP_ERROR if the copy
+ * fails.  Setting the environment variable CCL_SIM_DEBUG=1 makes every
+ * persistent call wait for its kernel and return CCL_SIM_HIP_ERROR itself
+ * when it aborted.
  * CCL_SIM_SPIN_LIMIT=n sets the poll limit (default 2^22); a tiny value
  * forces the abort from the host, for tests of this path.  Both are read
  * on every call.

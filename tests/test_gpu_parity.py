@@ -604,3 +604,30 @@ def test_ring_large_ragged_steps_every_element(cs, schedule):
             assert torch.equal(gathered[r][c * q:hi].view(torch.int32), want_dev), f"gathered: rank {r}, chunk {c}"
     del ar, shards, gathered
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n,q,dtype", [(64, 1000, "float32"), (256, 311, "bfloat16"), (256, 16384, "float32"),
+                                       (8, 3 * 16384 + 5, "int32")])
+def test_persistent_ring_repeats_match_the_stepwise_ring(cs, n, q, dtype):
+    """The persistent ring on small steps reads other workgroups' partials
+    through agent-coherent loads, with no cache maintenance at its grid
+    barrier.  Repeated calls on the same buffers (new data each time) must
+    give the stepwise ring's result, bit for bit, on every rank."""
+    m = n * q - 3
+    ws = cs.Workspace.largest([("allreduce", n, m, dtype, s) for s in ("ring_stepwise", "ring_persistent")])
+    for rep in range(6):
+        xs = U.random_inputs(n, m, dtype, seed=900 + rep)
+        send = U.bufs_from(xs, dtype)
+        got = [U.empty(m, dtype) for _ in range(n)]
+        want = [U.empty(m, dtype) for _ in range(n)]
+        cs.ccl_sim_allreduce(send, got, m, schedule="ring_persistent", workspace=ws, dtype=dtype)
+        torch.cuda.synchronize()
+        assert cs.ccl_sim_persistent_aborted(ws) is False  # before another call reuses the workspace
+        cs.ccl_sim_allreduce(send, want, m, schedule="ring_stepwise", workspace=ws, dtype=dtype)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(got[r], want[r]) if dtype == "int32" else \
+                torch.equal(got[r].view(torch.int16 if dtype == "bfloat16" else torch.int32),
+                            want[r].view(torch.int16 if dtype == "bfloat16" else torch.int32)), (rep, r)
+        if rep == 0:
+            assert U.same_bits(U.to_host(want[0], dtype), G.ring_allreduce(xs, "sum", dtype)[0])
