@@ -124,8 +124,10 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
     if info is None:
         raise SystemExit("no counters-pass record in " + pass_out)
     fetch, write = _counter(fetch_csv), _counter(write_csv)
-    fscale = info["copy_read_bytes"] / (fetch["pad_kernel"][0] * 1024)
-    wscale = info["copy_write_bytes"] / (write["pad_kernel"][0] * 1024)
+    # the pass makes one padding call; above 64 ranks it is several
+    # dispatches (one per 64-rank group), so the calibration sums them all
+    fscale = info["copy_read_bytes"] / (sum(fetch["pad_kernel"]) * 1024)
+    wscale = info["copy_write_bytes"] / (sum(write["pad_kernel"]) * 1024)
     rec = {}
     for kernel, algo in info["calls"].items():
         if len(fetch[kernel]) != len(write[kernel]):
@@ -150,8 +152,14 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
             "source_digest": info["kernel_source_digests"][kernel],
             "command": command,
         }
+    # one file holds every workload's records: replace this workload's, keep the others
+    merged = {}
+    if os.path.exists(out_json):
+        with open(out_json) as f:
+            merged = {k: v for k, v in json.load(f).items() if not k.endswith(":" + workload)}
+    merged.update(rec)
     with open(out_json, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(dict(sorted(merged.items())), f, indent=1)
         f.write("\n")
     _traffic_md(rec, workload, info, fscale, wscale, out_md, command)
     return rec

@@ -118,3 +118,27 @@ def test_traffic_scales_each_counter_by_the_plain_copy(tmp_path):
     assert rs["traffic_bytes"] == rs["call_traffic_bytes"] / 2
     assert json.loads((tmp_path / "t.json").read_text()) == rec
     assert "`rs_direct_kernel` | 2 |" in (tmp_path / "t.md").read_text()
+
+
+def test_traffic_calibrates_on_every_padding_dispatch_and_merges_workloads(tmp_path):
+    """Above 64 ranks the calibration's one padding call is several
+    dispatches: the scale uses their sum.  A second workload's records join
+    the first's in the same file instead of replacing them."""
+    header = ["Kernel_Name", "Counter_Value"]
+    fetch = [[PAD, 128.0], [PAD, 128.0], [PAD, 128.0], [PAD, 128.0], [AG, 64.0]]
+    write = [[PAD, 256.0], [PAD, 256.0], [PAD, 256.0], [PAD, 256.0], [AG, 1024.0]]
+    _write_csv(tmp_path / "f.csv", header, fetch)
+    _write_csv(tmp_path / "w.csv", header, write)
+    info = {"counters_pass": True, "copy_read_bytes": 1 << 20, "copy_write_bytes": 1 << 20,
+            "calls": {"ag_direct_kernel": 9 * 128 * 1024},
+            "kernel_source_digests": {"ag_direct_kernel": "a" * 16, "pad_kernel": "c" * 16}}
+    (tmp_path / "pass.out").write_text(json.dumps(info) + "\n")
+    out = tmp_path / "t.json"
+    out.write_text(json.dumps({"ag_direct_kernel:other": {"traffic_bytes": 1.0}}))
+    rec = profiling.traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "pass.out"), "w",
+                            str(out), str(tmp_path / "t.md"), "cmd")
+    ag = rec["ag_direct_kernel:w"]
+    assert ag["fetch_scale"] == pytest.approx(2.0) and ag["write_scale"] == pytest.approx(1.0)
+    assert ag["traffic_over_algorithmic"] == pytest.approx(1.0)
+    merged = json.loads(out.read_text())
+    assert set(merged) == {"ag_direct_kernel:other", "ag_direct_kernel:w"}
