@@ -50,6 +50,28 @@ def _run(cmd, verbose):
         print("\n".join(noise), file=sys.stderr)
 
 
+C_CHECK = os.path.join(ROOT, "tests", "c", "abi_gpu_check.c")
+C_CHECK_EXE = os.path.join(ROOT, "tests", "c", "abi_gpu_check")
+
+
+def build_c_check(verbose=False):
+    """The plain-C GPU check of the C ABI (tests/c/abi_gpu_check.c), linked
+    against the in-tree library with a relative run path, so that it runs
+    wherever the tree is copied.  Skipped without gcc."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        return None
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_CHECK_EXE + ".tmp"
+    _run([gcc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CHECK, "-o", tmp,
+          "-L", HERE, "-lccl_sim", "-Wl,-rpath,$ORIGIN/../../collective_reduction_amd",
+          "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")], verbose)
+    os.replace(tmp, C_CHECK_EXE)
+    return C_CHECK_EXE
+
+
 def build(extra_flags=(), output=LIB, verbose=False, jobs=None):
     """Compile every source and link ``output``; raises on failure."""
     jobs = jobs or min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
@@ -67,3 +89,4 @@ def build(extra_flags=(), output=LIB, verbose=False, jobs=None):
 
 if __name__ == "__main__":
     print(build(sys.argv[1:], verbose=True))
+    print(build_c_check(verbose=True))
