@@ -233,7 +233,9 @@ def _marshal(bufs, need, code, what, dev=None):
     return (ctypes.c_void_p * len(ptrs))(*ptrs), dev
 
 
-def _ws(workspace):
+def _ws(workspace, dev=None):
+    """(address, bytes) of the workspace.  A tensor must be a contiguous
+    device tensor on the call's device (`dev`, when the call has read it)."""
     if workspace is None:
         return ctypes.c_void_p(0), 0
     if isinstance(workspace, Workspace):
@@ -243,6 +245,8 @@ def _ws(workspace):
     if isinstance(workspace, torch.Tensor):
         if workspace.device.type != "cuda" or not workspace.is_contiguous():
             raise ValueError("the workspace must be a contiguous device tensor")
+        if dev is not None and workspace.get_device() != dev:
+            raise ValueError(f"the workspace is on {workspace.device}, not on the current device cuda:{dev}")
         return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
     addr, nbytes = workspace
     return ctypes.c_void_p(int(addr)), int(nbytes)
@@ -257,7 +261,7 @@ def ccl_sim_reduce_scatter(sendbufs, recvbufs, sendcount, recvcount, op="sum", s
     code = _infer_dtype(sendbufs, dtype)
     s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
     r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     _check(_reduce_scatter(s, r, n, sendcount, recvcount, code, _enum(OPS, op, "op"),
                            _enum(SCHEDULES, schedule, "schedule"), wp, wb, _stream(stream, dev)))
 
@@ -271,7 +275,7 @@ def ccl_sim_all_gather(sendbufs, recvbufs, sendcount, recvcount, schedule="direc
     code = _infer_dtype(sendbufs, dtype)
     s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
     r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     _check(_all_gather(s, r, n, sendcount, recvcount, code, _enum(SCHEDULES, schedule, "schedule"), wp, wb,
                        _stream(stream, dev)))
 
@@ -285,7 +289,7 @@ def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", wo
     code = _infer_dtype(sendbufs, dtype)
     s, dev = _marshal(sendbufs, count, code, "sendbufs")
     r, dev = _marshal(recvbufs, count, code, "recvbufs", dev)
-    wp, wb = _ws(workspace)
+    wp, wb = _ws(workspace, dev)
     _check(_allreduce(s, r, n, count, code, _enum(OPS, op, "op"), _enum(SCHEDULES, schedule, "schedule"), wp, wb,
                       _stream(stream, dev)))
 
@@ -332,7 +336,7 @@ class Plan:
             raise ValueError(f"{coll} needs both counts")
         s, dev = _marshal(sendbufs, sendcount, code, "sendbufs")
         r, dev = _marshal(recvbufs, recvcount, code, "recvbufs", dev)
-        wp, wb = _ws(workspace)
+        wp, wb = _ws(workspace, dev)
         self._dev = dev
         self._keep = (sendbufs, recvbufs, workspace, s, r)
         sched = _enum(SCHEDULES, schedule, "schedule")
@@ -441,7 +445,10 @@ class Workspace:
     @staticmethod
     def largest(requests, device="cuda"):
         """One workspace big enough for every (coll, nranks, count, dtype, schedule) request."""
+        sizes = [ccl_sim_workspace_size(*r) for r in requests]
+        if not sizes or ctypes.c_size_t(-1).value in sizes:
+            raise ValueError("invalid or empty workspace requests")
         w = Workspace.__new__(Workspace)
-        w.nbytes = max(ccl_sim_workspace_size(*r) for r in requests)
+        w.nbytes = max(sizes)
         w.tensor = torch.empty(max(w.nbytes, 1), dtype=torch.uint8, device=device) if w.nbytes else None
         return w

@@ -178,6 +178,20 @@ def test_workspace_sizes(cs):
     assert ws("allreduce", 0, 100, "float32", "direct") == ctypes.c_size_t(-1).value
 
 
+def test_workspace_objects_refuse_invalid_requests(cs):
+    """No allocation is attempted for a request the library calls invalid."""
+    with pytest.raises(ValueError, match="invalid"):
+        cs.Workspace("allreduce", 0, 100, "float32", "direct", device="cpu")
+    with pytest.raises(ValueError, match="invalid"):
+        cs.Workspace.largest([("allreduce", 8, 100, "float32", "direct"),
+                              ("allreduce", 2000, 100, "float32", "direct")], device="cpu")
+    with pytest.raises(ValueError, match="empty"):
+        cs.Workspace.largest([], device="cpu")
+    # sizes of zero need no tensor at all
+    w = cs.Workspace.largest([("allreduce", 8, 100, "float32", "direct")], device="cpu")
+    assert w.nbytes == 0 and w.tensor is None
+
+
 def test_algorithmic_bytes(cs):
     ab = cs.ccl_sim_algorithmic_bytes
     n, m = 8, 1 << 28
