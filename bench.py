@@ -30,6 +30,9 @@ import sys
 import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+# The headline: N=8 virtual ranks of 2^28 float32 elements (1 GiB each).
+DEFAULT_WORKLOAD = "uniform_8x268435456_fp32"
+METRIC = "effective HBM GB/s (and % of peak) for RS+AG AllReduce, N=8, M=2^28 fp32"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
 
 
@@ -42,7 +45,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="uniform_8x268435456_fp32")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--secondary-iters", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle work for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -307,7 +310,8 @@ def main():
         log(f"oracle: {cpu['value']:.3f} GB/s over {cpu['seconds']:.1f} s")
 
     out = {
-        "metric": "effective HBM GB/s (and % of peak) for RS+AG AllReduce, N=8, M=2^28 fp32",
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
+                  f"effective HBM GB/s (and % of peak) for RS+AG AllReduce, N={n}, M={m} {dtype}",
         "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
