@@ -444,6 +444,11 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
             cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule=s, workspace=ws, stream=stream),
             cs.ccl_sim_all_gather(shards, recv, q, m, schedule=s, workspace=ws, stream=stream)),
             ab("reduce_scatter", n, m, dtype, sched) + ab("all_gather", n, m, dtype, sched)))
+    # the direct pair again, interleaved with the direct AllReduce for the latency ratio below
+    cases.append(("rs_ag_direct", lambda: (
+        cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", stream=stream),
+        cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", stream=stream)),
+        ab("reduce_scatter", n, m, dtype, "direct") + ab("all_gather", n, m, dtype, "direct")))
     for sched in ("direct",) + RING_AND_RECURSIVE:
         cases.append((f"allreduce_{sched}", lambda s=sched: cs.ccl_sim_allreduce(
             send, recv, m, schedule=s, workspace=ws, stream=stream), ab("allreduce", n, m, dtype, sched)))
@@ -473,7 +478,21 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
             context[name] = (cs, "all_reduce", n, mm * es)
         elif name == "rs_only_direct":
             context[name] = (cs, "reduce_scatter", n, m * es)
-    return time_interleaved(torch, stream, cases, iters, context)
+    res = time_interleaved(torch, stream, cases, iters, context)
+    res["ratio_rs_ag_over_allreduce_direct"] = latency_ratio(res, "rs_ag_direct", "allreduce_direct", (n + 1) / n)
+    return res
+
+
+def latency_ratio(res, num, den, bytes_ratio):
+    """Median latency of `num` over that of `den`, timed interleaved, with
+    the ratio of their algorithmic bytes beside it.  Only stated when both
+    CVs are at most 5 %; otherwise the ratio is null and the CVs say why."""
+    a, b = res.get(num, {}), res.get(den, {})
+    if "median_ms" not in a or "median_ms" not in b:
+        return None
+    ok = a["cv"] <= 0.05 and b["cv"] <= 0.05
+    return {"of": f"{num} / {den}", "ratio": a["median_ms"] / b["median_ms"] if ok else None,
+            "cv": [a["cv"], b["cv"]], "bytes_ratio": bytes_ratio}
 
 
 def run_more_workloads(cs, torch, stream, iters):

@@ -142,3 +142,13 @@ def test_traffic_calibrates_on_every_padding_dispatch_and_merges_workloads(tmp_p
     assert ag["traffic_over_algorithmic"] == pytest.approx(1.0)
     merged = json.loads(out.read_text())
     assert set(merged) == {"ag_direct_kernel:other", "ag_direct_kernel:w"}
+
+
+def test_latency_ratio_is_stated_only_when_both_cvs_are_small():
+    res = {"a": {"median_ms": 3.0, "cv": 0.01}, "b": {"median_ms": 2.5, "cv": 0.02},
+           "noisy": {"median_ms": 2.0, "cv": 0.08}, "failed": {"error": "refused"}}
+    r = bench.latency_ratio(res, "a", "b", 9 / 8)
+    assert r["ratio"] == 3.0 / 2.5 and r["bytes_ratio"] == 9 / 8 and r["of"] == "a / b"
+    assert bench.latency_ratio(res, "a", "noisy", 1.0)["ratio"] is None
+    assert bench.latency_ratio(res, "a", "failed", 1.0) is None
+    assert bench.latency_ratio(res, "a", "missing", 1.0) is None
