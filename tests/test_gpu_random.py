@@ -6,7 +6,13 @@ dtype, an op, a schedule, a collective, the in-place form or not, and a
 base-address offset; the library's result must equal the oracle's in the
 schedule's combining order, bit for bit.  The draws come from one fixed
 seed, so a failure names a case that can be rerun exactly.
+
+CCL_SIM_TEST_RANDOM_SEED and CCL_SIM_TEST_RANDOM_BLOCKS (default 20261202
+and 8 blocks of 60 cases) widen the sweep: another seed draws other shapes,
+and its inputs are seeded apart from the default's (from 500000 on).
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -22,6 +28,10 @@ pytestmark = pytest.mark.gpu
 RANKS = (1, 2, 3, 4, 5, 7, 8, 13, 16, 31, 64, 65, 100, 128, 256)
 DTYPES = ("int32", "int64", "float32", "bfloat16")
 OPS = ("sum", "prod", "max", "min", "avg")
+DEFAULT_SEED = 20261202
+SEED = int(os.environ.get("CCL_SIM_TEST_RANDOM_SEED", DEFAULT_SEED))
+BLOCKS = int(os.environ.get("CCL_SIM_TEST_RANDOM_BLOCKS", 8))
+INPUT_BASE = 0 if SEED == DEFAULT_SEED else 500000
 
 
 @pytest.fixture(scope="module")
@@ -94,13 +104,13 @@ def run_case(cs, c, seed):
     return all(U.same_bits(y, want) for y in got)
 
 
-@pytest.mark.parametrize("block", range(8))
+@pytest.mark.parametrize("block", range(BLOCKS))
 def test_random_call_shapes(cs, block):
     """60 seeded cases per block; every failing case is listed."""
-    rng = np.random.default_rng([20261202, block])
+    rng = np.random.default_rng([SEED, block])
     failed = []
     for i in range(60):
         c = draw(rng)
-        if not run_case(cs, c, seed=1000 * block + i):
+        if not run_case(cs, c, seed=INPUT_BASE + 1000 * block + i):
             failed.append((i, c))
     assert not failed, f"cases that differ from the oracle: {failed}"
