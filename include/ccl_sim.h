@@ -24,7 +24,10 @@
  *            pointers; element r belongs to virtual rank r.  The caller
  *            allocates and owns every device buffer, including `workspace`.
  *            The library keeps no pointer after a call returns and allocates
- *            no device memory.
+ *            no device memory.  The kernels run on the calling thread's
+ *            current HIP device, so every rank buffer and the workspace must
+ *            be memory of that device (the library cannot check this: it
+ *            sees plain addresses).
  * Layout.    Every rank buffer is a contiguous 1-D array of `dtype`
  *            elements.  Element i of a full buffer belongs to shard i / q
  *            (rank-major sharding, [DECOMP] §数学证明).
