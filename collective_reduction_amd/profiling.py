@@ -179,8 +179,10 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
         "Commands (from `/tmp` with `TMPDIR=/tmp`; `<repo>` is the repository root):",
         "",
         "```",
-        f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py --counters-pass",
-        f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py --counters-pass",
+        f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py "
+        f"--workload {workload} --counters-pass",
+        f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py "
+        f"--workload {workload} --counters-pass",
         command,
         "```",
         "",
