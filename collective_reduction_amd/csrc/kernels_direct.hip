@@ -85,19 +85,21 @@ __device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t
   }
 }
 
-// The same copy with the fan-out split between two halves of a 512-lane
-// workgroup: both halves load the tile (the second load is served by the
-// caches), and half h stores outputs h·N/2 .. (h+1)·N/2 - 1, so each wave
-// issues half as many stores per tile.  Measured at N=8 on the same
-// buffers against one 256-lane workgroup storing all eight copies: 5.8 ->
-// 6.15 TB/s at M = 2^28 float32, 7 % faster in bf16, 5-8 % at M = 2^24 and
-// 2^26, 3 % at N = 16, even at N = 4.  The tile is the 256-lane tile of
-// AgPolicy, so both kernels share the grid and the ragged-tile bounds.
-template <class T>
-__device__ inline void ag_tile_halves(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
+// The same copy with the fan-out split between H parts of a 256·H-lane
+// workgroup: every part loads the tile (the later loads are served by the
+// caches), and part h stores outputs h·N/H .. (h+1)·N/H - 1, so each wave
+// issues 1/H of the stores per tile.  With H = 2, measured at N = 8 on the
+// same buffers against one 256-lane workgroup storing all eight copies:
+// 5.8 -> 6.15 TB/s at M = 2^28 float32, 7 % faster in bf16, 5-8 % at
+// M = 2^24 and 2^26, 3 % at N = 16, even at N = 4, and 18 % slower at
+// N = 2, where each half stores a single copy; with H = 4 it fell to
+// 4.7 TB/s at N = 8.  The tile is the 256-lane tile of AgPolicy, so both
+// kernels share the grid and the ragged-tile bounds.
+template <class T, int H>
+__device__ inline void ag_tile_parts(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
   constexpr int V = vec_elems<T>();
   constexpr uint64_t kTile = tile_of<AgPolicy>(V);
-  static_assert(AgPolicy::TB == 256 && AgPolicy::U == 1, "a half is one 256-lane, one-vector tile");
+  static_assert(AgPolicy::TB == 256 && AgPolicy::U == 1, "a part is one 256-lane, one-vector tile");
   using S = typename T::S;
   using SV = typename VecOf<S, V>::type;
   const int h = static_cast<int>(threadIdx.x) / 256, l = static_cast<int>(threadIdx.x) % 256;
@@ -106,7 +108,7 @@ __device__ inline void ag_tile_halves(const ShardArgs& a, int s, uint64_t seg, u
   const S* src = in_ptr<T>(a.send, s) + t0;
   if (t0 + kTile <= len) {
     const SV v = vload<S, V, AgPolicy::NTL>(src + uint64_t(l) * V);
-    const int k0 = h * a.nranks / 2, k1 = (h + 1) * a.nranks / 2;
+    const int k0 = h * a.nranks / H, k1 = (h + 1) * a.nranks / H;
     for (int k = k0; k < k1; ++k)
       store_through(out_ptr<T>(a.recv, k) + base + t0, uint32_t(kTile * sizeof(S)),
                     uint32_t(l * V * static_cast<int>(sizeof(S))), v);
@@ -124,9 +126,18 @@ __device__ inline void ag_tile_halves(const ShardArgs& a, int s, uint64_t seg, u
   }
 }
 
-// H = 1: 256-lane workgroups, each storing all N copies of its tile (one
-// rank, and from 64 ranks up, where the rotated fan-out order matters);
-// H = 2: 512-lane workgroups split into halves (2 <= N < 64).
+// Parts per AllGather workgroup for CCL_SIM_AG_PARTS_FROM <= N < 64 (each
+// part a 256-lane tile copy).
+#ifndef CCL_SIM_AG_PARTS
+#define CCL_SIM_AG_PARTS 2
+#endif
+#ifndef CCL_SIM_AG_PARTS_FROM
+#define CCL_SIM_AG_PARTS_FROM 4
+#endif
+
+// H = 1: 256-lane workgroups, each storing all N copies of its tile (below
+// CCL_SIM_AG_PARTS_FROM ranks, and from 64 up, where the rotated fan-out
+// order matters); H > 1: 256·H-lane workgroups split into H parts.
 template <class T, int H>
 __global__ __launch_bounds__(AgPolicy::TB * H) void ag_direct_kernel(ShardArgs a) {
   constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
@@ -135,8 +146,8 @@ __global__ __launch_bounds__(AgPolicy::TB * H) void ag_direct_kernel(ShardArgs a
     const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
     const uint64_t base = uint64_t(s) * a.q;
     const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
-    if constexpr (H == 2) {
-      ag_tile_halves<T>(a, s, seg, len);
+    if constexpr (H > 1) {
+      ag_tile_parts<T, H>(a, s, seg, len);
     } else if ((seg + 1) * kTile <= len) {
       ag_tile<T, true>(a, s, seg, len, first_output(tile, a.nranks));
     } else {
@@ -233,8 +244,9 @@ hipError_t run_direct(const Call& c) {
     if (c.coll == kAllGather) {
       const ShardArgs a = shard_args<AgPolicy, T>(c);
       const unsigned grid = grid_for(a.ntiles, c.num_cus);
-      if (c.nranks >= 2 && c.nranks < CCL_SIM_ROTATE_FROM)
-        hipLaunchKernelGGL((ag_direct_kernel<T, 2>), dim3(grid), dim3(2 * AgPolicy::TB), 0, c.stream, a);
+      if (c.nranks >= CCL_SIM_AG_PARTS_FROM && c.nranks < CCL_SIM_ROTATE_FROM)
+        hipLaunchKernelGGL((ag_direct_kernel<T, CCL_SIM_AG_PARTS>), dim3(grid), dim3(CCL_SIM_AG_PARTS * AgPolicy::TB), 0,
+                           c.stream, a);
       else
         hipLaunchKernelGGL((ag_direct_kernel<T, 1>), dim3(grid), dim3(AgPolicy::TB), 0, c.stream, a);
       return hipGetLastError();
