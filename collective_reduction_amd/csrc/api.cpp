@@ -111,11 +111,19 @@ Layout layout(int coll, int nranks, uint64_t m, int dtype, int schedule) {
 
 std::atomic<int> g_cus[64];
 
+// Largest persistent-ring grid, in workgroups per CU, that a call may ask
+// for.  Grids of 1 to 4 per CU have run to completion on MI355X in every
+// measurement; a grid at the occupancy calculator's figure (7 per CU) once
+// ran its first grid barrier into the poll limit, and why is not known, so
+// nothing above the largest grid seen to work is launched.
+constexpr int kMaxPersistentPerCu = 4;
+
 // Environment knobs (read on every call; see env()).
 //   CCL_SIM_DEBUG=1                      log each launch plan to stderr; after a
 //                                        persistent ring, wait for it and report a
 //                                        barrier that hit its poll limit
-//   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU
+//   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU, 1..4
+//                                        (anything else is refused before a launch)
 //   CCL_SIM_SPIN_LIMIT=n                 persistent ring barrier poll limit
 struct Env {
   bool debug = false;
@@ -211,17 +219,24 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (!valid_sched(schedule)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid schedule %d", schedule);
   if (recursive(schedule) && !pow2(nranks))
     return fail(CCL_SIM_UNSUPPORTED, "the recursive halving schedule needs a power-of-two nranks (got %d)", nranks);
+  const Env knobs = env();
+  if (effective_schedule(nranks, schedule) == CCL_SIM_RING_PERSISTENT &&
+      (knobs.per_cu < 0 || knobs.per_cu > kMaxPersistentPerCu))
+    return fail(CCL_SIM_UNSUPPORTED,
+                "CCL_SIM_PERSISTENT_BLOCKS_PER_CU=%d: the persistent ring runs 1 to %d workgroups per CU (0 = the "
+                "default); larger grids are not known to be co-resident",
+                knobs.per_cu, kMaxPersistentPerCu);
   const size_t es = elem_size(dtype);
 
   // Counts ([DECOMP] §源码一 count rules; §Contract 实验四 capacity check).
   uint64_t m = 0, q = 0, in_len = 0, out_len = 0;
   if (coll == CCL_SIM_COLL_REDUCE_SCATTER) {
     uint64_t need = 0;
+    // The capacity check of [DECOMP] §Contract 实验四: every rank's input
+    // must hold exactly one recvcount-element shard per rank.
     if (__builtin_mul_overflow(uint64_t(recvcount), uint64_t(nranks), &need) || need != sendcount)
-      return fail(CCL_SIM_CAPACITY_MISMATCH,
-                  "input tensor must be the same size as output size times world size "
-                  "(sendcount=%zu, nranks=%d, recvcount=%zu)",
-                  sendcount, nranks, recvcount);
+      return fail(CCL_SIM_CAPACITY_MISMATCH, "sendcount (%zu) != nranks (%d) x recvcount (%zu)", sendcount, nranks,
+                  recvcount);
     m = sendcount;
     q = recvcount;
     in_len = sendcount;
@@ -295,7 +310,6 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (lay.partial != SIZE_MAX) c.partial = ws + lay.partial;
   if (lay.ctrl != SIZE_MAX) c.ctrl = reinterpret_cast<unsigned*>(ws + lay.ctrl);
   c.stream = stream;
-  const Env knobs = env();
   c.persistent_per_cu = knobs.per_cu;
   c.spin_limit = knobs.spin_limit;
   c.log_plan = knobs.debug;

@@ -404,12 +404,13 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
     *unsupported = true;
     return hipSuccess;
   }
-  // Workgroups per CU: at most what the occupancy calculation allows, and
-  // by default only CCL_SIM_PERSISTENT_PER_CU of them.  A grid at the full
-  // occupancy figure was found not to be co-resident on MI355X (its first
-  // barrier ran into the poll limit); of the grids that are, one workgroup
-  // per CU measured fastest, at every step size: the barrier's cost grows
-  // with the number of workgroups that arrive.
+  // Workgroups per CU: the caller's request (the front end refuses more than
+  // four, the largest grid seen to complete), at most what the occupancy
+  // calculation allows, and by default CCL_SIM_PERSISTENT_PER_CU.  A grid
+  // at the full occupancy figure (7 per CU) once ran its first barrier into
+  // the poll limit, for a reason not established.  Of the grids that
+  // complete, one workgroup per CU measured fastest at every step size: the
+  // barrier's cost grows with the number of workgroups that arrive.
   const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
   const int use = want < per_cu ? want : per_cu;
   uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);

@@ -130,7 +130,11 @@ typedef enum {
    * between steps.  CCL_SIM_UNSUPPORTED when the device cannot keep the
    * grid resident, or when the runtime refuses the cooperative launch (ROCm
    * does, for instance, while another process on the same GPU holds its
-   * cooperative launch resources); the other schedules are unaffected. */
+   * cooperative launch resources); the other schedules are unaffected.
+   * The grid is one workgroup per CU unless the environment variable
+   * CCL_SIM_PERSISTENT_BLOCKS_PER_CU asks for 1 to 4; any other value
+   * (negative, or above 4, where co-residency is not established) makes
+   * the call return CCL_SIM_UNSUPPORTED before anything is enqueued. */
   CCL_SIM_RING_PERSISTENT = 2,
   /* Recursive-halving ReduceScatter and recursive-doubling AllGather
    * ([RS-PAGE] §Recursive Halving ReduceScatter): log2 N steps per phase, one

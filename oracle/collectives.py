@@ -40,6 +40,13 @@ def shard_count(count, nranks):
     return -(-count // nranks)
 
 
+def check_capacity(sendcount, nranks, recvcount):
+    """The ReduceScatter capacity rule ([DECOMP] §Contract 实验四): a rank's
+    input holds exactly one recvcount-element shard per rank, else TypeError."""
+    if sendcount != nranks * recvcount:
+        raise TypeError(f"sendcount ({sendcount}) != nranks ({nranks}) x recvcount ({recvcount})")
+
+
 def pad_identity(xs, op, dtype, padded_count):
     """Copy each rank's M elements and fill up to ``padded_count`` with the
     identity of ``op`` ([DECOMP] condition three: the pad value is the
@@ -76,14 +83,13 @@ def direct_allreduce(xs, op, dtype):
 def reduce_scatter(xs, op, dtype, recvcount):
     """Rank-major ReduceScatter with sendcount = N·recvcount (ascending order).
 
-    Raises TypeError, as the capacity check in [DECOMP] §Contract 实验四 does
-    ("input tensor must be the same size as output size times world size"),
-    when the input length is not exactly N·recvcount.
+    Raises TypeError, the exception the capacity check in [DECOMP]
+    §Contract 实验四 raises, when an input's length is not exactly
+    N·recvcount.
     """
     n = len(xs)
     for x in xs:
-        if np.asarray(x).size != n * recvcount:
-            raise TypeError("input tensor must be the same size as output size times world size")
+        check_capacity(np.asarray(x).size, n, recvcount)
     full = R.narrow(R.finalize(op, fold(xs, op, dtype, list(range(n))), n), dtype)
     return [full[r * recvcount:(r + 1) * recvcount].copy() for r in range(n)]
 

@@ -26,7 +26,7 @@ Readings where the page is silent:
 import numpy as np
 
 from . import reduction as R
-from .collectives import shard_count, pad_identity
+from .collectives import check_capacity, shard_count, pad_identity
 
 
 def _check_pow2(n):
@@ -101,8 +101,7 @@ def reduce_scatter(xs, op, dtype, recvcount, record=False):
     """Recursive-halving ReduceScatter with sendcount = N·recvcount."""
     n = len(xs)
     for x in xs:
-        if np.asarray(x).size != n * recvcount:
-            raise TypeError("input tensor must be the same size as output size times world size")
+        check_capacity(np.asarray(x).size, n, recvcount)
     q = recvcount
     bufs = [R.widen(x, dtype) for x in xs]
     states = _rh_phase(bufs, op, q, record)

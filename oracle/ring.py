@@ -45,7 +45,7 @@ completed chunk is stored.
 import numpy as np
 
 from . import reduction as R
-from .collectives import shard_count, pad_identity
+from .collectives import check_capacity, shard_count, pad_identity
 
 
 def reduce_scatter_route(nranks, step, rank):
@@ -149,8 +149,7 @@ def ring_reduce_scatter(xs, op, dtype, recvcount, record=False):
     """
     n = len(xs)
     for x in xs:
-        if np.asarray(x).size != n * recvcount:
-            raise TypeError("input tensor must be the same size as output size times world size")
+        check_capacity(np.asarray(x).size, n, recvcount)
     q = recvcount
     bufs = [R.widen(x, dtype) for x in xs]
     states = _rs_phase(bufs, op, q, record)

@@ -55,7 +55,7 @@ def test_capacity_check_rejects_nondivisible_reduce_scatter(cs):
     """1003 elements over 4 ranks with recvcount 250 is rejected with the
     capacity-check message before anything runs."""
     n = 4
-    with pytest.raises(TypeError, match="input tensor must be the same size as output size times world size"):
+    with pytest.raises(TypeError, match=r"sendcount \(1003\) != nranks \(4\) x recvcount \(250\)"):
         cs.ccl_sim_reduce_scatter(fake(n, 1003, 8), fake(n, 250, 8, base=BASE * 3), 1003, 250, dtype="int64")
     with pytest.raises(TypeError):
         cs.ccl_sim_all_gather(fake(n, 10, 4), fake(n, 41, 4, base=BASE * 3), 10, 41, dtype="float32")
@@ -132,7 +132,7 @@ def test_plan_checks_at_creation_and_validates_at_run(cs):
         cs.Plan("broadcast", fake(4, 100, 4), fake(4, 100, 4, base=BASE * 3), 100, 100, dtype="float32")
     plan = cs.Plan("reduce_scatter", fake(4, 1003, 8), fake(4, 250, 8, base=BASE * 3), 1003, 250, dtype="int64")
     for _ in range(2):
-        with pytest.raises(TypeError, match="input tensor must be the same size"):
+        with pytest.raises(TypeError, match="sendcount"):
             plan.run()
 
 
@@ -308,3 +308,31 @@ def test_c_abi_from_plain_c(tmp_path, cs):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0 and run.stdout.strip() == "ok", run.stdout + run.stderr
+
+
+def test_persistent_grid_request_is_capped(cs, monkeypatch):
+    """CCL_SIM_PERSISTENT_BLOCKS_PER_CU above 4 (the largest grid seen to run
+    to completion) or below 0 is refused with CCL_SIM_UNSUPPORTED before any
+    HIP call, for the persistent ring only; accepted values pass validation
+    and reach the device query, which fails here without a GPU."""
+    n, m = 4, 1000
+    s, r = fake(n, m, 4), fake(n, m, 4, base=BASE * 3)
+    need = cs.ccl_sim_workspace_size("allreduce", n, m, "float32", "ring_persistent")
+    ws = (BASE * 7, need)
+    ar = cs.ccl_sim_allreduce
+    for bad in ("5", "7", "-1"):
+        monkeypatch.setenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU", bad)
+        assert code_of(ar, s, r, m, dtype="float32", schedule="ring_persistent", workspace=ws) == cs.UNSUPPORTED
+        assert "CCL_SIM_PERSISTENT_BLOCKS_PER_CU" in cs.ccl_sim_last_error()
+        # the knob belongs to the persistent ring: other schedules ignore it
+        got = code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise", workspace=ws)
+        assert got != cs.UNSUPPORTED
+    for good in ("0", "1", "4"):
+        monkeypatch.setenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU", good)
+        got = code_of(ar, s, r, m, dtype="float32", schedule="ring_persistent", workspace=ws)
+        assert got != cs.UNSUPPORTED
+        assert "CCL_SIM_PERSISTENT_BLOCKS_PER_CU" not in cs.ccl_sim_last_error()
+    # a single rank has nothing to exchange and runs the direct copy: no grid to cap
+    monkeypatch.setenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU", "9")
+    got = code_of(ar, s[:1], r[:1], m, dtype="float32", schedule="ring_persistent")
+    assert got != cs.UNSUPPORTED

@@ -109,7 +109,8 @@ def test_nondivisible_without_padding_rejected(golden):
     g = golden("padding_1003_over_4.json")
     n, m = g["nranks"], g["logical_count"]
     xs = [np.zeros(m, dtype=np.int64) for _ in range(n)]
-    with pytest.raises(TypeError, match=g["rejection_message"]):
+    assert g["rejection_exception"] == "TypeError"
+    with pytest.raises(TypeError, match="sendcount"):
         C.reduce_scatter(xs, "sum", "int64", g["unpadded_floor_shard"])
     with pytest.raises(TypeError):
         G.ring_reduce_scatter(xs, "sum", "int64", g["unpadded_floor_shard"])
