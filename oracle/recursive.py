@@ -97,6 +97,26 @@ def _rd_phase(bufs, q, record):
     return states
 
 
+def butterfly_fold(xs, op, dtype):
+    """The combining tree of the halving phase, applied to whole arrays.
+
+    Every block is reduced by the same tree (see the module docstring): the
+    first step pairs rank i with rank i + N/2, the next pairs those partials
+    at distance N/4, and so on down to distance 1, the partial of the lower
+    rank always on the left.  Returns the accumulator of that tree at every
+    position (before AVG's division and bf16 rounding), so that a result
+    can be checked at any length without stepping the ranks.
+    """
+    n = len(xs)
+    _check_pow2(n)
+    acc = [R.widen(x, dtype) for x in xs]
+    d = n // 2
+    while d >= 1:
+        acc = [R.combine(op, acc[i], acc[i + d]) for i in range(d)]
+        d //= 2
+    return acc[0]
+
+
 def reduce_scatter(xs, op, dtype, recvcount, record=False):
     """Recursive-halving ReduceScatter with sendcount = N·recvcount."""
     n = len(xs)

@@ -5,8 +5,6 @@ back as NumPy arrays in the oracle's representation (bf16 as uint16 bits)."""
 import numpy as np
 import torch
 
-from collective_reduction_amd import inputs as I
-
 TORCH = {"int32": torch.int32, "int64": torch.int64, "float32": torch.float32, "bfloat16": torch.bfloat16}
 NP = {"int32": np.int32, "int64": np.int64, "float32": np.float32, "bfloat16": np.uint16}
 SCHEDULES = ("direct", "ring_stepwise", "ring_persistent", "recursive", "ring_chained", "recursive_chained")
@@ -126,36 +124,3 @@ def same_bits(a, b):
     if a.dtype == np.float32:
         return np.array_equal(a.view(np.uint32), b.view(np.uint32))
     return np.array_equal(a, b)
-
-
-def upload_workload(s, rows=None, workers=16, offset=0):
-    """Device buffers of a named workload, one tensor per rank, filled rank by
-    rank from the seeded generator (host memory holds one rank at a time)."""
-    n = s["nranks"]
-    rows = range(n) if rows is None else rows
-    out = []
-    for r in rows:
-        host = I.rank_buffer(s, r, workers=workers)
-        b = empty(s["count"], s["dtype"], offset=offset)
-        b.copy_(to_dev(host, s["dtype"]))
-        out.append(b)
-        del host
-    return out
-
-
-def sample_positions(m, q, k, seed):
-    """k random positions in [0, m) plus every shard's first and last two."""
-    rng = np.random.default_rng(seed)
-    pos = set(rng.integers(0, m, k).tolist())
-    n = -(-m // q) if q else 0
-    for c in range(n):
-        for d in (0, 1, q - 2, q - 1):
-            i = c * q + d
-            if 0 <= i < m:
-                pos.add(i)
-    return np.array(sorted(pos), dtype=np.int64)
-
-
-def pick(t, positions, dtype):
-    idx = torch.from_numpy(positions).to(t.device)
-    return to_host(t[idx], dtype)

@@ -55,6 +55,8 @@ PINS = [
     lambda: Q.test_butterfly_order_float32(),
     lambda: Q.test_max_ties_keep_the_lower_ranks_partial(),
     lambda: Q.test_doubling_all_gather_and_trim(),
+    lambda: Q.test_butterfly_fold_is_the_bracketed_tree(),
+    lambda: Q.test_butterfly_fold_matches_the_stepped_ranks("float32", "max"),
 ]
 
 
@@ -176,6 +178,22 @@ def _error_over_abs_of_sum(y, xs, dtype):
     return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), np.finfo(np.float64).tiny)))
 
 
+def _butterfly_adjacent_pairs(xs, op, dtype):
+    acc = [R.widen(x, dtype) for x in xs]
+    while len(acc) > 1:
+        acc = [R.combine(op, acc[2 * i], acc[2 * i + 1]) for i in range(len(acc) // 2)]
+    return acc[0]
+
+
+def _butterfly_upper_left(xs, op, dtype):
+    acc = [R.widen(x, dtype) for x in xs]
+    d = len(acc) // 2
+    while d >= 1:
+        acc = [R.combine(op, acc[i + d], acc[i]) for i in range(d)]
+        d //= 2
+    return acc[0]
+
+
 _ORIG_FOLD = C.fold
 _ORIG_GATHER = C.all_gather
 _ORIG_COMBINE = R.combine
@@ -199,6 +217,8 @@ MUTANTS = {
     "halving combines upper rank on the left": (H, "_rh_phase", _rh_phase_upper_left),
     "doubling copies the receiver's own block": (H, "_rd_phase", _rd_phase_own_block),
     "tolerance measure divides by |sum| instead of sum of |x|": (R, "normalized_sum_error", _error_over_abs_of_sum),
+    "butterfly fold pairs neighbouring ranks first": (H, "butterfly_fold", _butterfly_adjacent_pairs),
+    "butterfly fold puts the upper rank on the left": (H, "butterfly_fold", _butterfly_upper_left),
 }
 
 

@@ -126,3 +126,63 @@ def test_doubling_all_gather_and_trim():
 def test_non_power_of_two_rejected():
     with pytest.raises(ValueError):
         H.halving_pairs(6)
+
+
+def test_butterfly_fold_is_the_bracketed_tree():
+    """butterfly_fold at N = 8 is ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)), one
+    binary32 addition at a time, at every position."""
+    n, m = 8, 257
+    rng = np.random.default_rng(14)
+    xs = [rng.uniform(-1, 1, m).astype(np.float32) for _ in range(n)]
+    got = H.butterfly_fold(xs, "sum", "float32")
+    f = S.f32
+    for i in range(m):
+        v = [float(x[i]) for x in xs]
+        want = f(f(f(v[0] + v[4]) + f(v[2] + v[6])) + f(f(v[1] + v[5]) + f(v[3] + v[7])))
+        assert np.float32(want).view(np.uint32) == got[i].view(np.uint32)
+
+
+@pytest.mark.parametrize("dtype", R.DTYPES)
+@pytest.mark.parametrize("op", R.OPS)
+def test_butterfly_fold_matches_the_stepped_ranks(dtype, op):
+    """The fold written as one tree over whole arrays gives, at every
+    position, what stepping the halving and doubling phases rank by rank
+    gives (a different route through the same pairs), for every op and
+    dtype, N = 1 .. 32, lengths with and without padding; signed zeros make
+    MAX / MIN ties visible."""
+    for n in (1, 2, 4, 8, 16, 32):
+        for m in (n * 3, n * 3 + 1, 1):
+            rng = np.random.default_rng([n, m, len(op), len(dtype)])
+            if dtype in ("int32", "int64"):
+                lo, hi = (-4, 5) if op == "prod" else (-1000, 1000)
+                xs = [rng.integers(lo, hi, m).astype(R.STORAGE[dtype]) for _ in range(n)]
+            else:
+                f = rng.uniform(-1, 1, m).astype(np.float32)
+                xs = []
+                for _ in range(n):
+                    f = rng.uniform(0.5, 1.5, m).astype(np.float32) if op == "prod" else \
+                        rng.uniform(-1, 1, m).astype(np.float32)
+                    f = np.where(rng.random(m) < 0.2, np.float32(0.0) * np.sign(f), f).astype(np.float32)
+                    xs.append((f.view(np.uint32) >> np.uint32(16)).astype(np.uint16) if dtype == "bfloat16" else f)
+            want = H.allreduce(xs, op, dtype)[0]
+            got = R.narrow(R.finalize(op, H.butterfly_fold(xs, op, dtype), n), dtype)
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (n, m)
+
+
+def test_butterfly_fold_is_neither_ascending_nor_ring_order():
+    """At N = 16 the tree differs from the ascending fold and from every
+    ring chunk order somewhere (float32 SUM), and stays within the
+    summation bound."""
+    from oracle import ring as G
+    n, m = 16, 4096
+    rng = np.random.default_rng(15)
+    xs = [rng.uniform(-1, 1, m).astype(np.float32) for _ in range(n)]
+    got = H.butterfly_fold(xs, "sum", "float32")
+    for order in [list(range(n))] + [G.chunk_order(n, c) for c in range(n)]:
+        assert not np.array_equal(C.fold(xs, "sum", "float32", order).view(np.uint32), got.view(np.uint32))
+    assert R.normalized_sum_error(got, xs, "float32") <= (n - 1) * 2.0 ** -24
+
+
+def test_butterfly_fold_rejects_non_powers_of_two():
+    with pytest.raises(ValueError):
+        H.butterfly_fold([np.zeros(3, np.float32)] * 6, "sum", "float32")
