@@ -20,14 +20,23 @@ the workload.  Prints exactly one JSON line on stdout; progress goes to
 stderr.
 """
 
-import argparse
-import hashlib
-import json
 import os
-import re
-import statistics
-import sys
-import time
+
+# The CPU baseline times the oracle on one core: pin NumPy's and any BLAS
+# thread pools to one thread before NumPy (or torch, which loads it) is
+# imported.  Nothing else here uses those pools; the input generator's
+# worker threads are Python threads.
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+             "NUMEXPR_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
+    os.environ[_var] = "1"
+
+import argparse  # noqa: E402
+import hashlib  # noqa: E402
+import json  # noqa: E402
+import re  # noqa: E402
+import statistics  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # The headline: N=8 virtual ranks of 2^28 float32 elements (1 GiB each).
@@ -90,6 +99,13 @@ def load_traffic(kernel, workload, path=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
     when none were taken for this kernel and workload or the kernel source
     has changed since."""
+    entry = load_traffic_entry(kernel, workload, path)
+    return entry.get("traffic_bytes") if entry else None
+
+
+def load_traffic_entry(kernel, workload, path=None):
+    """The committed counter record of one kernel on one workload, or None
+    when none was taken or the kernel's source has changed since."""
     path = path or os.path.join(HERE, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -99,7 +115,68 @@ def load_traffic(kernel, workload, path=None):
     entry = rec.get(f"{kernel}:{workload}")
     if not entry or entry.get("source_digest") != kernel_source_digest(kernel):
         return None
-    return entry.get("traffic_bytes")
+    return entry
+
+
+AR_KERNEL = {"direct": "ar_direct_kernel", "ring_stepwise": "ring_step_kernel",
+             "ring_persistent": "ring_persistent_kernel", "ring_chained": "ring_chained_kernel",
+             "recursive": "recursive_step_kernel", "recursive_chained": "recursive_chained_kernel"}
+ROW_WORKLOADS = {"256x4194304_fp32": "normal_256x4194304_fp32", "256x6553600_bf16": "normal_256x6553600_bf16"}
+
+
+def row_kernels(name, default_workload):
+    """(kernels, workload) whose committed counters cover one bench row, or
+    None: the AllReduce rows (one kernel each), the direct ReduceScatter
+    alone, and the direct RS+AG pair."""
+    workload = default_workload
+    for suffix, wl in ROW_WORKLOADS.items():
+        if name.endswith("_" + suffix):
+            name, workload = name[:-len(suffix) - 1], wl
+            break
+    else:
+        if "_m2^" in name or name.endswith("_bf16"):
+            return None
+    if name.startswith("allreduce_") and name[len("allreduce_"):] in AR_KERNEL:
+        return [AR_KERNEL[name[len("allreduce_"):]]], workload
+    if name == "rs_only_direct":
+        return ["rs_direct_kernel"], workload
+    if name == "rs_ag_direct":
+        return ["rs_direct_kernel", "ag_direct_kernel"], workload
+    return None
+
+
+def label_rows(rows, default_workload):
+    """Say what each timed row's rate is.  Every row gets `cv_over_5pct`
+    (its median is then not stable enough to compare against another
+    row's; [DECOMP] states no ratio past that spread) and `rate_kind`:
+    "hbm" where the row's bytes come from HBM, or "effective_cache_assisted"
+    for the chained drivers and the cache-resident workload, whose data is
+    partly served from the 256 MB Infinity Cache (a chained driver reads
+    each partial back soon after writing it), so that their fraction of the
+    HBM peak is an effective rate, not an HBM roofline fraction.  Rows
+    covered by committed rocprofv3 counters also get
+    `traffic_over_algorithmic`: L2-to-fabric bytes (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a plain copy) over algorithmic bytes.  Those
+    counters see Infinity Cache hits as fetches, so a ratio near 1 does not
+    show how much of a row came from HBM itself."""
+    for name, row in rows.items():
+        if not isinstance(row, dict):
+            continue
+        if "cv" in row:
+            row["cv_over_5pct"] = row["cv"] > 0.05
+        if "gbs" in row:
+            cached = "chained" in name or "cache_resident" in name
+            row["rate_kind"] = "effective_cache_assisted" if cached else "hbm"
+        cover = row_kernels(name, default_workload)
+        if cover is None:
+            continue
+        kernels, workload = cover
+        entries = [load_traffic_entry(k, workload) for k in kernels]
+        if all(entries):
+            traffic = sum(e["call_traffic_bytes"] for e in entries)
+            alg = sum(e["call_algorithmic_bytes"] for e in entries)
+            row["traffic_over_algorithmic"] = traffic / alg
+            row["traffic_source"] = [f"{k}:{workload}" for k in kernels]
 
 
 def stats(ms):
@@ -154,6 +231,12 @@ def cpu_baseline(spec, target_s):
     dt = total
     nbytes = 2 * (n + 1) * n * qs * es * passes
     threads = os.environ.get("OMP_NUM_THREADS")
+    pools = None
+    try:
+        from threadpoolctl import threadpool_info
+        pools = sorted({p.get("num_threads") for p in threadpool_info()})
+    except Exception:  # noqa: BLE001  (the report works without it)
+        pass
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -173,6 +256,7 @@ def cpu_baseline(spec, target_s):
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "omp_num_threads": threads,
+        "blas_pool_threads": pools,
         "cpu_model": model,
     }
 
@@ -221,6 +305,8 @@ def main():
 
     if args.counters_pass:
         counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype)
+        del send, shards, recv
+        release_device_memory(torch)
         return
 
     send_elem_size = send[0].element_size()
@@ -278,10 +364,12 @@ def main():
     secondary = {}
     if not args.no_secondary:
         secondary = run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, args.secondary_iters)
-        del send, shards, recv
-        torch.cuda.empty_cache()
+    del send, shards, recv
+    release_device_memory(torch)
+    if not args.no_secondary:
         secondary.update(run_more_workloads(cs, torch, stream, args.secondary_iters))
         secondary.update(run_small(cs, torch, stream))
+        label_rows(secondary, args.workload)
 
     # Modeled context only (not a measurement, not a target): the pages'
     # α-β model of the same collective between N real ranks on their two
@@ -340,7 +428,19 @@ def main():
         "device": dev_name,
         "kernel_source_digest": kernel_source_digest(dominant[0]),
     }
+    release_device_memory(torch)
     print(json.dumps(out), flush=True)
+
+
+def release_device_memory(torch):
+    """Wait for the device and hand every cached block back to the runtime,
+    so that nothing allocated here is still alive when the process exits
+    (at exit the HIP runtime, and a profiler's library when one is loaded,
+    tear down in an order this program does not control)."""
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
@@ -463,7 +563,9 @@ def run_secondary(cs, torch, stream, send, shards, recv, n, m, q, dtype, iters):
         sv = [t[:mm] for t in send]
         rv = [t[:mm] for t in recv]
         hv = [t[:qq] for t in shards]
-        for sched in ("direct", "ring_stepwise", "ring_chained", "recursive_chained"):
+        for sched in ("direct",) + RING_AND_RECURSIVE:
+            if sched.startswith("recursive") and n & (n - 1):
+                continue
             cases.append((f"rs_ag_{sched}_m2^{lg}", lambda s=sched, sv=sv, rv=rv, hv=hv, mm=mm, qq=qq: (
                 cs.ccl_sim_reduce_scatter(sv, hv, mm, qq, schedule=s, workspace=ws, stream=stream),
                 cs.ccl_sim_all_gather(hv, rv, qq, mm, schedule=s, workspace=ws, stream=stream)),
