@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libccl_sim.so")
 HOST_SOURCES = ["api.cpp", "model.cpp"]
-KERNEL_SOURCES = ["kernels_direct.hip", "kernels_ring.hip", "kernels_recursive.hip", "kernels_misc.hip"]
+KERNEL_SOURCES = ["kernels_direct.hip", "kernels_ring.hip", "kernels_recursive.hip", "kernels_misc.hip", "scratch.hip"]
 SOURCES = [os.path.join(CSRC, s) for s in HOST_SOURCES + KERNEL_SOURCES]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -76,6 +76,9 @@ _all_gather = _sig("ccl_sim_all_gather", ctypes.c_int,
 _allreduce = _sig("ccl_sim_allreduce", ctypes.c_int,
                   [_vpp, _vpp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                    ctypes.c_void_p, _c_size, ctypes.c_void_p])
+_allreduce_noalloc = _sig("ccl_sim_allreduce_noalloc", ctypes.c_int,
+                          [_vpp, _vpp, ctypes.c_int, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_void_p])
 _pad_identity = _sig("ccl_sim_pad_identity", ctypes.c_int,
                      [_vpp, _vpp, ctypes.c_int, _c_size, _c_size, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
 _workspace_size = _sig("ccl_sim_workspace_size", _c_size,
@@ -119,7 +122,8 @@ EXPORTED = ("ccl_sim_reduce_scatter", "ccl_sim_all_gather", "ccl_sim_allreduce",
             "ccl_sim_workspace_size", "ccl_sim_algorithmic_bytes", "ccl_sim_launch_count", "ccl_sim_ring_owner",
             "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version",
             "ccl_sim_model_estimate", "ccl_sim_busbw_factor", "ccl_sim_recursive_route",
-            "ccl_sim_persistent_aborted")
+            "ccl_sim_persistent_aborted", "ccl_sim_allreduce_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CCL_SIM_NOALLOC_SCRATCH_BYTES
 
 
 class CclSimError(RuntimeError):
@@ -292,6 +296,21 @@ def ccl_sim_allreduce(sendbufs, recvbufs, count, op="sum", schedule="direct", wo
     wp, wb = _ws(workspace, dev)
     _check(_allreduce(s, r, n, count, code, _enum(OPS, op, "op"), _enum(SCHEDULES, schedule, "schedule"), wp, wb,
                       _stream(stream, dev)))
+
+
+def ccl_sim_allreduce_noalloc(sendbufs, recvbufs, count, op="sum", schedule="direct", stream=None, dtype=None):
+    """AllReduce with the library's own device scratch instead of a
+    workspace: the call allocates nothing (for graph capture and loops that
+    must not allocate).  Calls that overlap in time on one GPU race on its
+    scratch; see ccl_sim.h for the size limit."""
+    n = len(sendbufs)
+    if len(recvbufs) != n:
+        raise ValueError("sendbufs and recvbufs must list the same ranks")
+    code = _infer_dtype(sendbufs, dtype)
+    s, dev = _marshal(sendbufs, count, code, "sendbufs")
+    r, dev = _marshal(recvbufs, count, code, "recvbufs", dev)
+    _check(_allreduce_noalloc(s, r, n, count, code, _enum(OPS, op, "op"), _enum(SCHEDULES, schedule, "schedule"),
+                              _stream(stream, dev)))
 
 
 def ccl_sim_pad_identity(srcs, dsts, count, padded_count, op, stream=None, dtype=None):

@@ -14,8 +14,6 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
-#include <string>
-#include <vector>
 
 #include "ccl_sim.h"
 #include "internal.hpp"
@@ -24,19 +22,23 @@ namespace {
 
 using namespace ccl;
 
-thread_local std::string g_last_error;
+// The last failure's message, per thread.  The validation path keeps to
+// fixed buffers (this one, and the rank spans on the stack), so that no
+// call allocates memory of any kind on the host either.
+constexpr int kMessageBytes = 512;
+thread_local char g_last_error[kMessageBytes];
+
+void clear_error() { g_last_error[0] = '\0'; }
 
 // Records the message for ccl_sim_last_error() and returns `code`.  A HIP
 // failure is reported through the returned code, so HIP's own last-error
 // slot is cleared as well: left set, it would resurface in the caller's
 // next, unrelated HIP call.
 ccl_sim_result_t fail(ccl_sim_result_t code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   if (code == CCL_SIM_HIP_ERROR) (void)hipGetLastError();
   return code;
 }
@@ -166,24 +168,25 @@ struct Span {
 
 // Outputs must be pairwise disjoint; an input may overlap an output only
 // when they belong to the same rank and `allowed(rank)` says the pair is the
-// in-place form.  O(N log N).
+// in-place form.  Sorts `outs` (n_outs spans) in place; on failure the
+// reason is recorded with fail().  O(N log N).
 template <class Allowed>
-bool overlap_ok(std::vector<Span> outs, const std::vector<Span>& ins, Allowed allowed, std::string* why) {
-  outs.erase(std::remove_if(outs.begin(), outs.end(), [](const Span& s) { return s.hi == s.lo; }), outs.end());
-  std::sort(outs.begin(), outs.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
-  for (size_t i = 1; i < outs.size(); ++i)
-    if (outs[i - 1].hi > outs[i].lo) {
-      *why = "output buffers of ranks " + std::to_string(outs[i - 1].rank) + " and " + std::to_string(outs[i].rank) +
-             " overlap";
+bool overlap_ok(Span* outs, int n_outs, const Span* ins, int n_ins, Allowed allowed) {
+  Span* end = std::remove_if(outs, outs + n_outs, [](const Span& s) { return s.hi == s.lo; });
+  std::sort(outs, end, [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (Span* o = outs + 1; o < end; ++o)
+    if (o[-1].hi > o->lo) {
+      fail(CCL_SIM_INVALID_ARGUMENT, "output buffers of ranks %d and %d overlap", o[-1].rank, o->rank);
       return false;
     }
-  for (const Span& in : ins) {
+  for (int i = 0; i < n_ins; ++i) {
+    const Span& in = ins[i];
     if (in.hi == in.lo) continue;
-    auto it = std::upper_bound(outs.begin(), outs.end(), in.lo, [](uintptr_t v, const Span& s) { return v < s.hi; });
-    for (; it != outs.end() && it->lo < in.hi; ++it) {
+    const Span* it = std::upper_bound(outs, end, in.lo, [](uintptr_t v, const Span& s) { return v < s.hi; });
+    for (; it != end && it->lo < in.hi; ++it) {
       if (it->rank != in.rank || !allowed(in.rank)) {
-        *why = "input of rank " + std::to_string(in.rank) + " overlaps the output of rank " +
-               std::to_string(it->rank) + " outside the in-place form";
+        fail(CCL_SIM_INVALID_ARGUMENT, "input of rank %d overlaps the output of rank %d outside the in-place form",
+             in.rank, it->rank);
         return false;
       }
     }
@@ -191,9 +194,9 @@ bool overlap_ok(std::vector<Span> outs, const std::vector<Span>& ins, Allowed al
   return true;
 }
 
-bool spans_clear_of(const std::vector<Span>& spans, uintptr_t lo, uintptr_t hi) {
-  for (const Span& s : spans)
-    if (s.hi > s.lo && s.lo < hi && lo < s.hi) return false;
+bool spans_clear_of(const Span* spans, int n, uintptr_t lo, uintptr_t hi) {
+  for (int i = 0; i < n; ++i)
+    if (spans[i].hi > spans[i].lo && spans[i].lo < hi && lo < spans[i].hi) return false;
   return true;
 }
 
@@ -211,7 +214,7 @@ ccl_sim_result_t check_ptrs(const void* const* ptrs, int nranks, const char* wha
 ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* const* recvbufs, int nranks,
                                 size_t sendcount, size_t recvcount, int dtype, int op, int schedule, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS)
     return fail(CCL_SIM_INVALID_ARGUMENT, "nranks=%d outside [1, %d]", nranks, CCL_SIM_MAX_RANKS);
   if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", dtype);
@@ -266,7 +269,7 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   rc = check_ptrs(const_cast<const void* const*>(recvbufs), nranks, "recvbufs", es);
   if (rc != CCL_SIM_SUCCESS) return rc;
 
-  std::vector<Span> ins(nranks), outs(nranks);
+  Span ins[CCL_SIM_MAX_RANKS], outs[CCL_SIM_MAX_RANKS];
   for (int r = 0; r < nranks; ++r) {
     const uintptr_t s = reinterpret_cast<uintptr_t>(sendbufs[r]);
     const uintptr_t d = reinterpret_cast<uintptr_t>(recvbufs[r]);
@@ -279,8 +282,10 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     if (coll == CCL_SIM_COLL_REDUCE_SCATTER) return d == s + uint64_t(r) * q * es;
     return s == d + uint64_t(r) * q * es;
   };
-  std::string why;
-  if (!overlap_ok(outs, ins, in_place, &why)) return fail(CCL_SIM_INVALID_ARGUMENT, "%s", why.c_str());
+  // in_place() reads the spans' original order: sort a copy of the outputs
+  Span sorted_outs[CCL_SIM_MAX_RANKS];
+  std::copy(outs, outs + nranks, sorted_outs);
+  if (!overlap_ok(sorted_outs, nranks, ins, nranks, in_place)) return CCL_SIM_INVALID_ARGUMENT;
 
   const int sched = effective_schedule(nranks, schedule);
   const Layout lay = layout(coll, nranks, m, dtype, schedule);
@@ -291,7 +296,7 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
                   workspace == nullptr ? size_t(0) : workspace_bytes, workspace == nullptr ? " (NULL)" : "");
     const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
     if (w % kAlign != 0) return fail(CCL_SIM_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if (!spans_clear_of(ins, w, w + lay.total) || !spans_clear_of(outs, w, w + lay.total))
+    if (!spans_clear_of(ins, nranks, w, w + lay.total) || !spans_clear_of(outs, nranks, w, w + lay.total))
       return fail(CCL_SIM_INVALID_ARGUMENT, "workspace overlaps a rank buffer");
   }
 
@@ -405,10 +410,40 @@ ccl_sim_result_t ccl_sim_allreduce(const void* const* sendbufs, void* const* rec
                         workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
+ccl_sim_result_t ccl_sim_allreduce_noalloc(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                           size_t count, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
+                                           ccl_sim_schedule_t schedule, ccl_sim_stream_t stream) {
+  clear_error();
+  if (count == 0) return CCL_SIM_SUCCESS;  // nothing to compute, scratch untouched
+  if (nranks >= 1 && nranks <= CCL_SIM_MAX_RANKS && valid_dtype(dtype) && valid_sched(schedule) &&
+      !(recursive(schedule) && !pow2(nranks))) {
+    if (effective_schedule(nranks, schedule) == CCL_SIM_RING_PERSISTENT)
+      return fail(CCL_SIM_UNSUPPORTED,
+                  "the persistent ring is not offered without a workspace: its abort word could not be queried");
+    const Layout lay = layout(CCL_SIM_COLL_ALLREDUCE, nranks, count, dtype, schedule);
+    if (!lay.ok || lay.total > CCL_SIM_NOALLOC_SCRATCH_BYTES)
+      return fail(CCL_SIM_INSUFFICIENT_WORKSPACE,
+                  "this call needs a workspace of %zu bytes; the library's scratch holds %zu",
+                  lay.ok ? lay.total : SIZE_MAX, CCL_SIM_NOALLOC_SCRATCH_BYTES);
+    if (lay.total > 0) {
+      void* scratch = nullptr;
+      size_t bytes = 0;
+      const hipError_t e = noalloc_scratch(&scratch, &bytes);
+      if (e != hipSuccess)
+        return fail(CCL_SIM_HIP_ERROR, "reading the scratch's device address failed: %s", hipGetErrorString(e));
+      return run_collective(CCL_SIM_COLL_ALLREDUCE, sendbufs, recvbufs, nranks, count, count, dtype, op, schedule,
+                            scratch, bytes, reinterpret_cast<hipStream_t>(stream));
+    }
+  }
+  // no scratch needed, or invalid arguments (which run_collective reports)
+  return run_collective(CCL_SIM_COLL_ALLREDUCE, sendbufs, recvbufs, nranks, count, count, dtype, op, schedule, nullptr,
+                        0, reinterpret_cast<hipStream_t>(stream));
+}
+
 ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts, int nranks, size_t count,
                                       size_t padded_count, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
                                       ccl_sim_stream_t stream) {
-  g_last_error.clear();
+  clear_error();
   if (nranks < 1 || nranks > CCL_SIM_MAX_RANKS)
     return fail(CCL_SIM_INVALID_ARGUMENT, "nranks=%d outside [1, %d]", nranks, CCL_SIM_MAX_RANKS);
   if (!valid_dtype(dtype)) return fail(CCL_SIM_INVALID_ARGUMENT, "invalid dtype %d", int(dtype));
@@ -427,18 +462,18 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
   }
   rc = check_ptrs(const_cast<const void* const*>(dsts), nranks, "dsts", es);
   if (rc != CCL_SIM_SUCCESS) return rc;
-  std::vector<Span> ins, outs(nranks);
+  Span ins[CCL_SIM_MAX_RANKS], outs[CCL_SIM_MAX_RANKS];
+  int n_ins = 0;
   for (int r = 0; r < nranks; ++r) {
     const uintptr_t d = reinterpret_cast<uintptr_t>(dsts[r]);
     outs[r] = Span{d, d + padded_count * es, r};
     if (count > 0) {
       const uintptr_t s = reinterpret_cast<uintptr_t>(srcs[r]);
-      ins.push_back(Span{s, s + count * es, r});
+      ins[n_ins++] = Span{s, s + count * es, r};
     }
   }
-  std::string why;
   auto same = [&](int r) { return count == 0 || srcs[r] == dsts[r]; };
-  if (!overlap_ok(outs, ins, same, &why)) return fail(CCL_SIM_INVALID_ARGUMENT, "%s", why.c_str());
+  if (!overlap_ok(outs, nranks, ins, n_ins, same)) return CCL_SIM_INVALID_ARGUMENT;
 
   Call c;
   c.dtype = dtype;
@@ -576,10 +611,10 @@ const char* ccl_sim_result_string(ccl_sim_result_t result) {
   }
 }
 
-const char* ccl_sim_last_error(void) { return g_last_error.c_str(); }
+const char* ccl_sim_last_error(void) { return g_last_error; }
 
 ccl_sim_result_t ccl_sim_persistent_aborted(const void* workspace, int* aborted) {
-  g_last_error.clear();
+  clear_error();
   if (workspace == nullptr || aborted == nullptr)
     return fail(CCL_SIM_INVALID_ARGUMENT, "workspace and aborted must not be NULL");
   // The control block opens the persistent ring's workspace (layout()).

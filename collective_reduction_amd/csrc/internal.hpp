@@ -67,6 +67,10 @@ hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded);
 // arguments carry them; no host-to-device memcpy).
 hipError_t upload_table(const void** dev_table, const void* const* host_ptrs, int n, hipStream_t stream);
 
+// Device address and size of the current device's library-owned scratch
+// (scratch.hip), read once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 size_t elem_size(int dtype);
 size_t accum_size(int dtype);
 

@@ -91,6 +91,9 @@ extern "C" {
 #define CCL_SIM_VERSION 100      /* 1.0.0 */
 #define CCL_SIM_MAX_RANKS 1024
 #define CCL_SIM_INLINE_RANKS 64  /* up to this many ranks need no pointer table in the workspace */
+/* Size of the library's own device scratch used by ccl_sim_allreduce_noalloc
+ * (64 MiB per GPU the library runs on). */
+#define CCL_SIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum {
   CCL_SIM_SUCCESS = 0,
@@ -221,6 +224,38 @@ ccl_sim_result_t ccl_sim_all_gather(const void* const* sendbufs, void* const* re
 ccl_sim_result_t ccl_sim_allreduce(const void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                                    ccl_sim_dtype_t dtype, ccl_sim_op_t op, ccl_sim_schedule_t schedule,
                                    void* workspace, size_t workspace_bytes, ccl_sim_stream_t stream);
+
+/*
+ * ccl_sim_allreduce without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics, kernels and results as ccl_sim_allreduce with the
+ * same schedule; the workspace that call would need comes from a device
+ * array owned by the library, CCL_SIM_NOALLOC_SCRATCH_BYTES on each GPU,
+ * held from the first call on that GPU until the process ends.  The call
+ * itself allocates nothing, on the device or the host.
+ *
+ * Limits and errors, all checked before anything is enqueued:
+ *   - a call whose ccl_sim_workspace_size(CCL_SIM_COLL_ALLREDUCE, ...)
+ *     exceeds CCL_SIM_NOALLOC_SCRATCH_BYTES returns
+ *     CCL_SIM_INSUFFICIENT_WORKSPACE (for float32 ring AllReduce that is
+ *     M of about 2^23 elements per rank; the direct schedule with at most
+ *     64 ranks needs no scratch at any size);
+ *   - CCL_SIM_RING_PERSISTENT returns CCL_SIM_UNSUPPORTED, since its abort
+ *     word would live where the caller cannot query it;
+ *   - everything else as for ccl_sim_allreduce.
+ * The first call on each device reads the scratch's device address (one
+ * hipGetSymbolAddress, which may load the library's code object): make it
+ * outside graph capture.  Every call on one GPU uses that GPU's one
+ * scratch, so calls that overlap in time on one GPU (on different streams,
+ * or from different threads) race on it and give undefined results; calls
+ * in stream order are safe.  Nothing in the scratch has to start at zero:
+ * every partial and pointer table is written before it is read, within
+ * the same call.
+ */
+ccl_sim_result_t ccl_sim_allreduce_noalloc(const void* const* sendbufs, void* const* recvbufs, int nranks,
+                                           size_t count, ccl_sim_dtype_t dtype, ccl_sim_op_t op,
+                                           ccl_sim_schedule_t schedule, ccl_sim_stream_t stream);
 
 /*
  * Identity padding ([DECOMP] §等价成立的条件, condition three):

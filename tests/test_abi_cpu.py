@@ -336,3 +336,32 @@ def test_persistent_grid_request_is_capped(cs, monkeypatch):
     monkeypatch.setenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU", "9")
     got = code_of(ar, s[:1], r[:1], m, dtype="float32", schedule="ring_persistent")
     assert got != cs.UNSUPPORTED
+
+
+def test_noalloc_allreduce_limits_are_checked_before_any_hip_call(cs):
+    """ccl_sim_allreduce_noalloc refuses the persistent ring and any call
+    whose workspace would not fit the library's scratch before touching the
+    device; count 0 is a no-op; invalid arguments are reported as by
+    ccl_sim_allreduce."""
+    n, m = 8, 1000
+    s, r = fake(n, m, 4), fake(n, m, 4, base=BASE * 3)
+    noalloc = cs.ccl_sim_allreduce_noalloc
+    assert code_of(noalloc, s, r, m, dtype="float32", schedule="ring_persistent") == cs.UNSUPPORTED
+    assert "persistent" in cs.ccl_sim_last_error()
+    # ring partials 2·N·q·4 bytes: the largest M that fits, and the next size up
+    cap = cs.NOALLOC_SCRATCH_BYTES
+    fits = cap // 8
+    assert cs.ccl_sim_workspace_size("allreduce", n, fits, "float32", "ring_stepwise") <= cap
+    too_big = fits + 8 * 64
+    assert cs.ccl_sim_workspace_size("allreduce", n, too_big, "float32", "ring_stepwise") > cap
+    big_s, big_r = fake(n, too_big, 4), fake(n, too_big, 4, base=BASE * 40)
+    assert code_of(noalloc, big_s, big_r, too_big, dtype="float32", schedule="ring_stepwise") == \
+        cs.INSUFFICIENT_WORKSPACE
+    assert "scratch" in cs.ccl_sim_last_error()
+    # the recursive halves N·(N/2)·q·a reach the limit sooner
+    assert code_of(noalloc, big_s, big_r, too_big, dtype="float32", schedule="recursive") == \
+        cs.INSUFFICIENT_WORKSPACE
+    cs.ccl_sim_allreduce_noalloc([0] * 4, [0] * 4, 0, dtype="float32", schedule="ring_stepwise")
+    assert code_of(noalloc, s, r, m, dtype="float32", op=9) == cs.INVALID_ARGUMENT
+    assert code_of(noalloc, s[:6], r[:6], m, dtype="float32", schedule="recursive") == cs.UNSUPPORTED
+    assert code_of(noalloc, [], [], m, dtype="float32") == cs.INVALID_ARGUMENT
