@@ -162,9 +162,9 @@ def label_rows(rows, default_workload):
     for name, row in rows.items():
         if not isinstance(row, dict):
             continue
-        if "cv" in row:
+        if isinstance(row.get("cv"), float):
             row["cv_over_5pct"] = row["cv"] > 0.05
-        if "gbs" in row:
+        if row.get("gbs") is not None:
             cached = "chained" in name or "cache_resident" in name
             row["rate_kind"] = "effective_cache_assisted" if cached else "hbm"
         cover = row_kernels(name, default_workload)

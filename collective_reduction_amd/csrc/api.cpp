@@ -121,9 +121,13 @@ std::atomic<int> g_cus[64];
 constexpr int kMaxPersistentPerCu = 4;
 
 // Environment knobs (read on every call; see env()).
-//   CCL_SIM_DEBUG=1                      log each launch plan to stderr; after a
-//                                        persistent ring, wait for it and report a
-//                                        barrier that hit its poll limit
+//   CCL_SIM_DEBUG=1                      log each launch plan to stderr; fill the
+//                                        partials' scratch with all-ones bits before
+//                                        a ring or recursive call, so a read of a
+//                                        partial before its write shows in the
+//                                        result; after a persistent ring, wait for
+//                                        it and report a barrier that hit its poll
+//                                        limit
 //   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU, 1..4
 //                                        (anything else is refused before a launch)
 //   CCL_SIM_SPIN_LIMIT=n                 persistent ring barrier poll limit
@@ -335,6 +339,11 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "pointer table upload failed: %s", hipGetErrorString(e));
     c.send.table = reinterpret_cast<const uint64_t*>(st);
     c.recv.table = reinterpret_cast<const uint64_t*>(rt);
+  }
+
+  if (c.log_plan && c.partial != nullptr) {
+    e = poison_fill(c.partial, lay.total - lay.partial, stream);
+    if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "scratch poison fill failed: %s", hipGetErrorString(e));
   }
 
   if (sched == CCL_SIM_DIRECT) {

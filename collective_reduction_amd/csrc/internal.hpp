@@ -67,6 +67,11 @@ hipError_t run_pad(const Call& c, uint64_t count, uint64_t padded);
 // arguments carry them; no host-to-device memcpy).
 hipError_t upload_table(const void** dev_table, const void* const* host_ptrs, int n, hipStream_t stream);
 
+// Debug check of the scratch (CCL_SIM_DEBUG): all-ones bits over `bytes`
+// (a multiple of 4) on the stream, before a schedule that keeps partials
+// there runs.
+hipError_t poison_fill(void* p, size_t bytes, hipStream_t stream);
+
 // Device address and size of the current device's library-owned scratch
 // (scratch.hip), read once per device.
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);

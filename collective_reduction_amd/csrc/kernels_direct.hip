@@ -156,6 +156,54 @@ __global__ __launch_bounds__(AgPolicy::TB * H) void ag_direct_kernel(ShardArgs a
   }
 }
 
+// The AllGather with its tile staged in LDS: the 256·H lanes of a workgroup
+// load a tile of 256·H vectors once, one vector per lane, and park it in
+// LDS; after a workgroup barrier, part h (256 lanes) stores the whole tile
+// into outputs h·N/H .. (h+1)·N/H - 1, H vectors per lane per output.  No
+// part reloads the tile, and each output receives 4·H KiB of contiguous
+// stores from one part.  The last, ragged tile of a shard is copied
+// element by element by all lanes.
+#ifndef CCL_SIM_AG_LDS_PARTS
+#define CCL_SIM_AG_LDS_PARTS 0
+#endif
+template <class T, int H>
+__global__ __launch_bounds__(256 * H) void ag_lds_kernel(ShardArgs a) {
+  using S = typename T::S;
+  constexpr int V = vec_elems<T>();
+  using SV = typename VecOf<S, V>::type;
+  constexpr int TB = 256 * H;
+  constexpr uint64_t kTile = uint64_t(TB) * V;
+  __shared__ SV stage[TB];
+  const int lane = static_cast<int>(threadIdx.x);
+  const int h = lane / 256, l = lane % 256;
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int s = rank_of_tile(tile, a.tiles_per_shard);
+    const uint64_t seg = tile - uint64_t(s) * a.tiles_per_shard;
+    const uint64_t base = uint64_t(s) * a.q;
+    const uint64_t len = base >= a.limit ? 0 : (a.limit - base < a.q ? a.limit - base : a.q);
+    const uint64_t t0 = seg * kTile;
+    const S* src = in_ptr<T>(a.send, s) + t0;
+    if (t0 + kTile <= len) {
+      stage[lane] = vload<S, V, AgPolicy::NTL>(src + uint64_t(lane) * V);
+      __syncthreads();
+      const int k0 = h * a.nranks / H, k1 = (h + 1) * a.nranks / H;
+      for (int k = k0; k < k1; ++k) {
+        S* dst = out_ptr<T>(a.recv, k) + base + t0;
+#pragma unroll
+        for (int i = 0; i < H; ++i)
+          store_through(dst, uint32_t(kTile * sizeof(S)), uint32_t((i * 256 + l) * int(sizeof(SV))), stage[i * 256 + l]);
+      }
+      __syncthreads();  // the next tile reuses the stage
+    } else {
+      const uint64_t end = len < t0 + kTile ? len : t0 + kTile;
+      for (uint64_t j = t0 + uint64_t(lane); j < end; j += TB) {
+        const S x = get1(src - t0 + j);
+        for (int k = 0; k < a.nranks; ++k) put1(out_ptr<T>(a.recv, k) + base + j, x);
+      }
+    }
+  }
+}
+
 struct FlatArgs {
   RankPtrs send, recv;
   int nranks;
@@ -195,6 +243,50 @@ __global__ __launch_bounds__(P::TB) void ar_direct_kernel(FlatArgs a) {
   }
 }
 
+// The direct AllReduce with the folded tile shared through LDS: each of
+// the 256·H lanes folds its own vector over the N inputs (ascending ranks,
+// as ar_tile does) and parks the result in LDS; after a workgroup barrier,
+// part h (256 lanes) stores the whole tile into outputs h·N/H ..
+// (h+1)·N/H - 1.  The barrier also orders the in-place form: every load of
+// the tile's positions, from every input, precedes the first store into
+// them.  The ragged last tile takes ar_tile's path (each lane stores its
+// own vector to every output).
+#ifndef CCL_SIM_AR_LDS_PARTS
+#define CCL_SIM_AR_LDS_PARTS 0
+#endif
+template <class T, int OP, int H>
+__global__ __launch_bounds__(256 * H) void ar_lds_kernel(FlatArgs a) {
+  using P = Policy<256 * H, 1, true, kStoreWriteThrough>;
+  using S = typename T::S;
+  constexpr int V = vec_elems<T>();
+  using SV = typename VecOf<S, V>::type;
+  constexpr uint64_t kTile = tile_of<P>(V);
+  __shared__ SV stage[P::TB];
+  const int lane = static_cast<int>(threadIdx.x);
+  const int h = lane / 256, l = lane % 256;
+  for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    if ((tile + 1) * kTile > a.count) {
+      ar_tile<T, OP, P, false>(a, tile);
+      continue;
+    }
+    using L = Lane<T, P, true>;
+    const L ln(tile, a.count);
+    typename T::A acc[1][V];
+    fold_ranks<T, OP, P, true>(a.send, a.nranks, 0, ln, acc);
+    stage[lane] = finish_vec<T, OP, SV>(acc[0], a.nranks);
+    __syncthreads();
+    const uint64_t t0 = tile * kTile;
+    const int k0 = h * a.nranks / H, k1 = (h + 1) * a.nranks / H;
+    for (int k = k0; k < k1; ++k) {
+      S* dst = out_ptr<T>(a.recv, k) + t0;
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+        store_through(dst, uint32_t(kTile * sizeof(S)), uint32_t((i * 256 + l) * int(sizeof(SV))), stage[i * 256 + l]);
+    }
+    __syncthreads();  // the next tile reuses the stage
+  }
+}
+
 }  // namespace
 
 // The fused reductions (ReduceScatter and AllReduce) take two vectors per
@@ -206,6 +298,18 @@ __global__ __launch_bounds__(P::TB) void ar_direct_kernel(FlatArgs a) {
 #ifndef CCL_SIM_DIRECT_SMALL_CALL
 #define CCL_SIM_DIRECT_SMALL_CALL (uint64_t(1) << 24)
 #endif
+
+template <class T, int OP, int H>
+hipError_t launch_ar_lds(const Call& c) {
+  FlatArgs a{};
+  a.send = c.send;
+  a.recv = c.recv;
+  a.nranks = c.nranks;
+  a.count = c.limit;
+  a.ntiles = ceil_div(c.limit, uint64_t(256 * H) * vec_elems<T>());
+  hipLaunchKernelGGL((ar_lds_kernel<T, OP, H>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(256 * H), 0, c.stream, a);
+  return hipGetLastError();
+}
 
 template <class T, int OP, class P>
 hipError_t launch_ar_direct(const Call& c) {
@@ -242,6 +346,15 @@ hipError_t launch_rs_direct(const Call& c) {
 hipError_t run_direct(const Call& c) {
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
     if (c.coll == kAllGather) {
+      if constexpr (CCL_SIM_AG_LDS_PARTS > 1) {
+        if (c.nranks >= CCL_SIM_AG_PARTS_FROM && c.nranks < CCL_SIM_ROTATE_FROM) {
+          using LP = Policy<256 * CCL_SIM_AG_LDS_PARTS, 1, true, kStoreWriteThrough>;
+          const ShardArgs a = shard_args<LP, T>(c);
+          hipLaunchKernelGGL((ag_lds_kernel<T, CCL_SIM_AG_LDS_PARTS>), dim3(grid_for(a.ntiles, c.num_cus)),
+                             dim3(LP::TB), 0, c.stream, a);
+          return hipGetLastError();
+        }
+      }
       const ShardArgs a = shard_args<AgPolicy, T>(c);
       const unsigned grid = grid_for(a.ntiles, c.num_cus);
       if (c.nranks >= CCL_SIM_AG_PARTS_FROM && c.nranks < CCL_SIM_ROTATE_FROM)
@@ -254,8 +367,11 @@ hipError_t run_direct(const Call& c) {
     const uint64_t produced = (c.coll == kAllReduce) ? c.limit : uint64_t(c.nranks) * c.q;
     const bool small = produced <= CCL_SIM_DIRECT_SMALL_CALL;
     return by_op<T>(c.op, [&]<class U, int OP>() -> hipError_t {
-      if (c.coll == kAllReduce)
+      if (c.coll == kAllReduce) {
+        if constexpr (CCL_SIM_AR_LDS_PARTS > 1)
+          if (!small && c.nranks >= CCL_SIM_AR_LDS_PARTS) return launch_ar_lds<U, OP, CCL_SIM_AR_LDS_PARTS>(c);
         return small ? launch_ar_direct<U, OP, DirectSmallPolicy>(c) : launch_ar_direct<U, OP, ArPolicy>(c);
+      }
       return small ? launch_rs_direct<U, OP, DirectSmallPolicy>(c) : launch_rs_direct<U, OP, RsPolicy>(c);
     });
   });

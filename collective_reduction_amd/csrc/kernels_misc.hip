@@ -127,4 +127,33 @@ hipError_t upload_table(const void** dev_table, const void* const* host_ptrs, in
   return hipSuccess;
 }
 
+namespace {
+
+// Fills `words` 32-bit words with all-ones bits, one 128-bit store per lane
+// per step plus a word-wise tail.  As a float32 the pattern is a NaN, as a
+// float32 partial of bf16 data too, and as an integer it is -1, so a result
+// that folded any word of it is visibly wrong.
+__global__ __launch_bounds__(256) void poison_kernel(unsigned* p, uint64_t words) {
+  using W4 = unsigned __attribute__((ext_vector_type(4)));
+  const uint64_t vecs = words / 4;
+  const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
+  W4 ones = {~0u, ~0u, ~0u, ~0u};
+  for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < vecs; i += stride)
+    *(CCL_GLOBAL W4*)(p + 4 * i) = ones;
+  for (uint64_t i = vecs * 4 + uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += stride)
+    *(CCL_GLOBAL unsigned*)(p + i) = ~0u;
+}
+
+}  // namespace
+
+hipError_t poison_fill(void* p, size_t bytes, hipStream_t stream) {
+  const uint64_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const uint64_t vecs = (words + 3) / 4;
+  const uint64_t blocks = (vecs + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(poison_kernel, dim3(grid), dim3(256), 0, stream, static_cast<unsigned*>(p), words);
+  return hipGetLastError();
+}
+
 }  // namespace ccl

@@ -59,7 +59,8 @@ __device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
 // in one state machine as in [DECOMP] §源码三), ReduceScatter into
 // recvbufs[c], c = r+1.
 template <class T, int OP, class P, bool FULL, bool CO>
-__device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len) {
+__device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len,
+                                    const typename Lane<T, P, FULL, CO>::SV* own_ahead = nullptr) {
   using A = typename T::A;
   using L = Lane<T, P, FULL, CO>;
   constexpr int V = vec_elems<T>();
@@ -90,7 +91,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
   }
 #pragma unroll
   for (int u = 0; u < P::U; ++u)
-    if (ln.on(u)) own[u] = ln.load(mine, u);
+    if (ln.on(u)) own[u] = own_ahead ? own_ahead[u] : ln.load(mine, u);
   if (!last) {
     A* dst = part + (a.chunk_keyed ? cbase : uint64_t(t & 1) * slot + uint64_t(r) * a.q);
 #pragma unroll
@@ -198,8 +199,11 @@ __global__ __launch_bounds__(P::TB) void ring_chained_kernel(RingArgs a) {
   }
 }
 
-// Grid-wide barrier for the persistent ring.  Every workgroup of the grid
-// is co-resident (cooperative launch) and arrives once per barrier.
+// Grid-wide barrier for the persistent ring, in two halves: grid_arrive
+// counts the workgroup in, grid_wait waits for the whole grid, and the
+// workgroup may issue loads that depend on no other workgroup in between.
+// Every workgroup of the grid is co-resident (cooperative launch) and
+// arrives once per barrier.
 //
 // Arrival is two-level: workgroup b counts itself on the counter of group
 // b mod kCtrlGroups (each counter on its own cache line), and the group's
@@ -225,13 +229,11 @@ __global__ __launch_bounds__(P::TB) void ring_chained_kernel(RingArgs a) {
 // word, and every workgroup that sees the word stops, so the grid always
 // drains.
 template <bool CO>
-__device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spin_limit) {
-  __shared__ int s_ok;
+__device__ inline void grid_arrive(unsigned* ctrl, unsigned epoch) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned grid = gridDim.x;
-    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
     const unsigned g = blockIdx.x % unsigned(kCtrlGroups);
     const unsigned members = (grid - g + kCtrlGroups - 1) / kCtrlGroups;
     if constexpr (!CO) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -241,6 +243,15 @@ __device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spi
       if constexpr (!CO) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
       __hip_atomic_fetch_add(ctrl + kCtrlBarrier, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+template <bool CO>
+__device__ inline bool grid_wait(unsigned* ctrl, unsigned epoch, unsigned spin_limit) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    const unsigned grid = gridDim.x;
+    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
     int ok = 1;
     unsigned spins = 0;
     while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch * groups) {
@@ -260,17 +271,75 @@ __device__ inline bool grid_barrier(unsigned* ctrl, unsigned epoch, unsigned spi
   return s_ok != 0;
 }
 
+// The ReduceScatter-phase tile a workgroup handles first at a step, and
+// whether it is a whole tile.
+struct RsTileAt {
+  int r = 0, c = 0;
+  uint64_t seg = 0, len = 0;
+  bool full = false;
+};
+template <class P, class T>
+__device__ inline RsTileAt rs_tile_at(const RingArgs& a, int step, uint64_t tile) {
+  constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
+  RsTileAt x;
+  x.r = rank_of_tile(tile, a.tiles_per_chunk);
+  x.seg = tile - uint64_t(x.r) * a.tiles_per_chunk;
+  x.c = mod_n(x.r - 1 - step, a.nranks);
+  x.len = chunk_len(a, x.c);
+  x.full = (x.seg + 1) * kTile <= x.len;
+  return x;
+}
+
+#ifndef CCL_SIM_PERSIST_AHEAD
+#define CCL_SIM_PERSIST_AHEAD 1
+#endif
+
 // CO: the data path is agent-coherent and the barrier does no cache
 // maintenance (chosen for small steps, where the barrier dominates; see
 // run_ring_persistent).
+//
+// The barrier is split into its arrival and its wait.  In between, a
+// workgroup whose next step is a ReduceScatter step loads the rank's own
+// input vectors of its first tile of that step: x^(r) is never written
+// during the call at a position the ReduceScatter phase still reads (the
+// in-place forms overwrite only chunks their rank has already folded, or
+// chunk r of rank r, which that rank never reads), so the loads need no
+// ordering against the other workgroups' stores, and their latency
+// overlaps the wait.  Measured at N = 256, M = 2^22 float32: 4.63 against
+// 4.81 ms.  Not for bf16, whose float32 partials already fill the register
+// budget of a 1024-lane workgroup (128 VGPRs): there the held vectors made
+// the call slower (5.78 against 5.41 ms at the 6,553,600-element bucket).
 template <class T, int OP, class P, bool CO>
 __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
+  using LF = Lane<T, P, true, CO>;
+  constexpr bool kAhead = CCL_SIM_PERSIST_AHEAD && sizeof(typename T::A) == sizeof(typename T::S);
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
   unsigned epoch = 0;
+  typename LF::SV ahead[P::U];
   for (int step = a.first_step; step < nsteps; ++step) {
-    if (step > a.first_step && !grid_barrier<CO>(a.ctrl, ++epoch, a.spin_limit)) return;
-    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) ring_body<T, OP, P, CO>(a, step, tile);
+    bool have_ahead = false;
+    RsTileAt first;
+    if (step > a.first_step) {
+      grid_arrive<CO>(a.ctrl, epoch + 1);
+      if (kAhead && a.coll != kAllGather && step < n - 1 && uint64_t(blockIdx.x) < a.ntiles) {
+        first = rs_tile_at<P, T>(a, step, blockIdx.x);
+        if (first.full) {
+          const LF ln(first.seg, first.len);
+          const typename T::S* mine = in_ptr<T>(a.send, first.r) + uint64_t(first.c) * a.q;
+#pragma unroll
+          for (int u = 0; u < P::U; ++u) ahead[u] = ln.load(mine, u);
+          have_ahead = true;
+        }
+      }
+      if (!grid_wait<CO>(a.ctrl, ++epoch, a.spin_limit)) return;
+    }
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+      if (have_ahead && tile == blockIdx.x)
+        ring_rs_tile<T, OP, P, true, CO>(a, step, first.r, first.seg, first.c, first.len, ahead);
+      else
+        ring_body<T, OP, P, CO>(a, step, tile);
+    }
   }
 }
 
@@ -411,7 +480,11 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
   // the poll limit, for a reason not established.  Of the grids that
   // complete, one workgroup per CU measured fastest at every step size: the
   // barrier's cost grows with the number of workgroups that arrive.
-  const int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
+  // Never more than 1024 lanes (16 waves) per CU: the largest grids seen to
+  // complete held four 256-lane or one 1024-lane workgroup per CU.
+  const int lanes_cap = 1024 / P::TB > 0 ? 1024 / P::TB : 1;
+  int want = c.persistent_per_cu > 0 ? c.persistent_per_cu : CCL_SIM_PERSISTENT_PER_CU;
+  want = want < lanes_cap ? want : lanes_cap;
   const int use = want < per_cu ? want : per_cu;
   uint64_t grid = uint64_t(use) * uint64_t(c.num_cus);
   if (grid > a.ntiles) grid = a.ntiles;

@@ -75,8 +75,15 @@
  *            CCL_SIM_RECURSIVE reduces each block as the butterfly tree of
  *            its halving steps.
  * Threads.   The library holds no mutable global state except a cached
- *            per-device compute-unit count and a thread-local error
- *            message; calls with distinct workspaces may run concurrently.
+ *            per-device compute-unit count, a thread-local error message
+ *            and the per-device scratch of ccl_sim_allreduce_noalloc; calls
+ *            with distinct workspaces may run concurrently.
+ * Debug.     With the environment variable CCL_SIM_DEBUG=1 (read on every
+ *            call) each call logs its launch plan to stderr, and before a
+ *            ring or recursive call that keeps partials in the workspace
+ *            the library fills their part of it with all-ones bits (a NaN
+ *            as float32, -1 as an integer) on the call's stream, so that a
+ *            partial read before it is written shows in the result.
  */
 #ifndef CCL_SIM_H
 #define CCL_SIM_H

@@ -152,3 +152,36 @@ def test_latency_ratio_is_stated_only_when_both_cvs_are_small():
     assert bench.latency_ratio(res, "a", "noisy", 1.0)["ratio"] is None
     assert bench.latency_ratio(res, "a", "failed", 1.0) is None
     assert bench.latency_ratio(res, "a", "missing", 1.0) is None
+
+
+def test_label_rows_on_every_row_shape():
+    """Timed rows get a CV flag and a rate kind; the chained drivers and
+    the cache-resident shape are labelled cache-assisted; rows with a list
+    of CVs (the latency ratio) or without a rate are left as they are;
+    rows covered by counters get their traffic ratio."""
+    rows = {
+        "allreduce_ring_stepwise": {"gbs": 5000.0, "cv": 0.01},
+        "rs_ag_direct": {"gbs": 6000.0, "cv": 0.07},
+        "allreduce_ring_chained_256x4194304_fp32": {"gbs": 6900.0, "cv": 0.0},
+        "rs_ag_direct_8x1048576_fp32_cache_resident": {"gbs": 3000.0, "calls": 100, "mean_ms": 0.02},
+        "ratio_rs_ag_over_allreduce_direct": {"of": "a / b", "ratio": None, "cv": [0.01, 0.09]},
+        "launch_floor_allreduce_direct_8x64": {"gbs": None, "calls": 100},
+        "rs_ag_ring_chained_m2^24": {"gbs": 7000.0, "cv": 0.02},
+        "broken": {"error": "refused"},
+        "ratio_missing": None,
+    }
+    bench.label_rows(rows, "uniform_8x268435456_fp32")
+    assert rows["allreduce_ring_stepwise"]["cv_over_5pct"] is False
+    assert rows["allreduce_ring_stepwise"]["rate_kind"] == "hbm"
+    assert rows["rs_ag_direct"]["cv_over_5pct"] is True
+    assert rows["allreduce_ring_chained_256x4194304_fp32"]["rate_kind"] == "effective_cache_assisted"
+    assert rows["rs_ag_ring_chained_m2^24"]["rate_kind"] == "effective_cache_assisted"
+    assert rows["rs_ag_direct_8x1048576_fp32_cache_resident"]["rate_kind"] == "effective_cache_assisted"
+    assert "cv_over_5pct" not in rows["ratio_rs_ag_over_allreduce_direct"]
+    assert rows["broken"] == {"error": "refused"}
+    assert "rate_kind" not in rows["launch_floor_allreduce_direct_8x64"]
+    assert bench.row_kernels("allreduce_ring_persistent_256x6553600_bf16", "w") == \
+        (["ring_persistent_kernel"], "normal_256x6553600_bf16")
+    assert bench.row_kernels("rs_ag_direct", "w") == (["rs_direct_kernel", "ag_direct_kernel"], "w")
+    assert bench.row_kernels("rs_ag_ring_chained_m2^24", "w") is None
+    assert bench.row_kernels("allreduce_direct_8x268435456_bf16", "w") is None
