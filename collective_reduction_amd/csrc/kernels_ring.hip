@@ -250,10 +250,10 @@ template <bool CO>
 __device__ inline bool grid_wait(unsigned* ctrl, unsigned epoch, unsigned spin_limit) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
-    const unsigned grid = gridDim.x;
-    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
     int ok = 1;
     unsigned spins = 0;
+    const unsigned grid = gridDim.x;
+    const unsigned groups = grid < unsigned(kCtrlGroups) ? grid : unsigned(kCtrlGroups);
     while (__hip_atomic_load(ctrl + kCtrlBarrier, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < epoch * groups) {
       if (++spins > spin_limit ||
           ((spins & 63u) == 0u &&
@@ -448,16 +448,23 @@ hipError_t run_ring_chained(const Call& c) {
 // is then one tile per workgroup) measured 9-17 % faster than 256 lanes;
 // for larger steps 256 lanes were faster.
 //
-// The same threshold picks the data path.  Small steps are dominated by
+// A second threshold picks the data path.  Small steps are dominated by
 // the barrier, and there the agent-coherent path, whose barrier does no
 // cache write-back or invalidation, measured 8-25 % faster (N = 256, M =
-// 2^22 float32: 4.87 against 6.51 ms).  Large steps are dominated by
-// streaming, and there the plain nontemporal loads of the fenced path were
-// faster (N = 8, M = 2^28: 6.52 against 7.04 ms).  Both gave results
-// bit-identical to the stepwise ring in every one of about a hundred
-// calls over eight shapes and three dtypes.
+// 2^22 float32: 4.87 against 6.51 ms; N = 8, M = 2^24, steps of 2^24
+// elements: 0.457 against 0.529 ms for RS + AG).  Larger steps are
+// dominated by streaming, and there the plain nontemporal loads of the
+// fenced path were faster: with the 1024-lane shape at N = 8, M = 2^26
+// (steps of 2^26 elements) 1.648 against 1.820 ms for RS + AG in float32
+// and 1.097 against 1.209 ms in bf16; with 256 lanes at M = 2^28, 6.52
+// against 7.04 ms.  Both paths gave results bit-identical to the stepwise
+// ring in every one of about a hundred calls over eight shapes and three
+// dtypes.
 #ifndef CCL_SIM_PERSIST_SMALL_STEP
 #define CCL_SIM_PERSIST_SMALL_STEP (uint64_t(1) << 26)
+#endif
+#ifndef CCL_SIM_PERSIST_COHERENT_STEP
+#define CCL_SIM_PERSIST_COHERENT_STEP (uint64_t(1) << 25)
 #endif
 
 template <class T, int OP, class P, bool CO>
@@ -497,7 +504,7 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
     plan->lanes = P::TB;
     plan->coherent = CO;
   }
-  hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(kCtrlWords), 0, c.stream, c.ctrl);
+  hipLaunchKernelGGL(reset_ctrl_kernel, dim3(1), dim3(256), 0, c.stream, c.ctrl);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   void* args[] = {&a};
@@ -523,10 +530,14 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan*
   *unsupported = false;
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
     const int op = (c.coll == kAllGather) ? int(kSum) : c.op;
-    const bool small = uint64_t(c.nranks) * c.q <= CCL_SIM_PERSIST_SMALL_STEP;
+    const uint64_t step = uint64_t(c.nranks) * c.q;
+    const bool small = step <= CCL_SIM_PERSIST_SMALL_STEP;
+    const bool coherent = step <= CCL_SIM_PERSIST_COHERENT_STEP;
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
-      return small ? launch_persistent<U, OP, PersistSmallPolicy, true>(c, unsupported, plan)
-                   : launch_persistent<U, OP, PersistPolicy, false>(c, unsupported, plan);
+      if (small)
+        return coherent ? launch_persistent<U, OP, PersistSmallPolicy, true>(c, unsupported, plan)
+                        : launch_persistent<U, OP, PersistSmallPolicy, false>(c, unsupported, plan);
+      return launch_persistent<U, OP, PersistPolicy, false>(c, unsupported, plan);
     });
   });
 }

@@ -493,15 +493,17 @@ def test_uniform_8x256m_fp32_every_element(cs, schedule):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("m", [(1 << 26) + 12345, (1 << 26) - 12345])
 @pytest.mark.parametrize("schedule", ["ring_stepwise", "ring_persistent", "ring_chained"])
-def test_ring_large_ragged_steps_every_element(cs, schedule):
-    """N=8 ring steps of about 2^26 float32 (the large-step launch shapes)
-    whose chunks end in a ragged tile under every launch shape (q =
-    8,390,152).  AllReduce of M = 2^26 + 12345 (virtual padding of 7) and
-    RS + AG of the padded length, every element against the oracle's fold
-    of chunk c in the ring's order."""
+def test_ring_large_ragged_steps_every_element(cs, schedule, m):
+    """N=8 ring steps of about 2^26 float32 whose chunks end in a ragged tile
+    under every launch shape: just above 2^26 elements per step (q =
+    8,390,152; the large-step launch shapes) and just below (q = 8,386,761;
+    the persistent ring's 1024-lane workgroups on its fenced data path).
+    AllReduce of M (virtual padding) and RS + AG of the padded length,
+    every element against the oracle's fold of chunk c in the ring's
+    order."""
     n = 8
-    m = (1 << 26) + 12345
     q = -(-m // n)
     xs = U.random_inputs(n, n * q, "float32", seed=31)
     send = [U.to_dev(x, "float32") for x in xs]
