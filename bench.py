@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--counters-pass", action="store_true",
                    help="run one RS, one AG and one plain copy of known size, for rocprofv3 --pmc")
+    p.add_argument("--counters-schedules", default=",".join(AR_KERNEL),
+                   help="the AllReduce schedules the counters pass runs (comma-separated)")
     return p.parse_args()
 
 
@@ -304,7 +306,7 @@ def main():
     torch.cuda.synchronize()
 
     if args.counters_pass:
-        counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype)
+        counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype, args.counters_schedules.split(","))
         del send, shards, recv
         release_device_memory(torch)
         return
@@ -443,25 +445,25 @@ def release_device_memory(torch):
     torch.cuda.empty_cache()
 
 
-def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
+def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype, schedules=tuple(AR_KERNEL)):
     """One call of each kernel the bench times, for hardware counters: the
     direct ReduceScatter and AllGather, ccl_sim_pad_identity with nothing to
     pad (a plain copy of N·M elements, reading and writing N·M·s bytes,
     which calibrates FETCH_SIZE / WRITE_SIZE against a known byte count),
-    then one AllReduce each with the direct, stepwise-ring, persistent-ring,
-    chained-ring and both recursive schedules (recursive only for a
-    power-of-two N)."""
+    then one AllReduce with each of `schedules` (by default the direct,
+    stepwise-ring, persistent-ring, chained-ring and both recursive
+    schedules; recursive only for a power-of-two N)."""
+    unknown = set(schedules) - set(AR_KERNEL)
+    if unknown:
+        raise SystemExit(f"unknown schedules {sorted(unknown)}")
     ws = cs.Workspace.largest([("reduce_scatter", n, m, dtype, "direct"), ("all_gather", n, m, dtype, "direct")])
     cs.ccl_sim_reduce_scatter(send, shards, m, q, schedule="direct", workspace=ws, stream=stream)
     cs.ccl_sim_all_gather(shards, recv, q, m, schedule="direct", workspace=ws, stream=stream)
     cs.ccl_sim_pad_identity(send, recv, m, m, "sum", stream=stream)
     calls = {"rs_direct_kernel": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct"),
              "ag_direct_kernel": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")}
-    for kernel, schedule in (("ar_direct_kernel", "direct"), ("ring_step_kernel", "ring_stepwise"),
-                             ("ring_persistent_kernel", "ring_persistent"), ("ring_chained_kernel", "ring_chained"),
-                             ("recursive_step_kernel", "recursive"),
-                             ("recursive_chained_kernel", "recursive_chained")):
-        if schedule.startswith("recursive") and n & (n - 1):
+    for schedule, kernel in AR_KERNEL.items():
+        if schedule not in schedules or (schedule.startswith("recursive") and n & (n - 1)):
             continue
         ws = cs.Workspace("allreduce", n, m, dtype, schedule)
         cs.ccl_sim_allreduce(send, recv, m, schedule=schedule, workspace=ws, stream=stream)
@@ -471,6 +473,7 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype):
     torch.cuda.synchronize()
     es = send[0].element_size()
     print(json.dumps({"counters_pass": True, "calls": calls,
+                      "counters_schedules_arg": None if set(schedules) >= set(AR_KERNEL) else ",".join(schedules),
                       "copy_read_bytes": n * m * es, "copy_write_bytes": n * m * es,
                       "kernel_source_digests": {k: kernel_source_digest(k) for k in list(calls) + ["pad_kernel"]}}),
           flush=True)

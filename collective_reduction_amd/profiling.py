@@ -124,6 +124,11 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
     if info is None:
         raise SystemExit("no counters-pass record in " + pass_out)
     fetch, write = _counter(fetch_csv), _counter(write_csv)
+    extra = info.get("counters_schedules_arg")
+    pass_commands = [f"rocprofv3 --pmc {c} --kernel-trace -d <out> -o pmc --output-format csv -- python "
+                     f"<repo>/bench.py --workload {workload} --counters-pass" + (f" --counters-schedules {extra}"
+                                                                                  if extra else "")
+                     for c in ("FETCH_SIZE", "WRITE_SIZE")]
     # the pass makes one padding call; above 64 ranks it is several
     # dispatches (one per 64-rank group), so the calibration sums them all
     fscale = info["copy_read_bytes"] / (sum(fetch["pad_kernel"]) * 1024)
@@ -151,21 +156,31 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
             "calibration": "ccl_sim_pad_identity with count == padded_count (plain copy of N*M elements)",
             "source_digest": info["kernel_source_digests"][kernel],
             "command": command,
+            "pass_commands": pass_commands,
         }
-    # one file holds every workload's records: replace this workload's, keep the others
+    # one file holds every workload's records: replace the kernels this pass
+    # measured on this workload, keep the rest (other workloads, and kernels
+    # of this workload that a pass over other schedules measured)
     merged = {}
     if os.path.exists(out_json):
         with open(out_json) as f:
-            merged = {k: v for k, v in json.load(f).items() if not k.endswith(":" + workload)}
+            merged = {k: v for k, v in json.load(f).items() if k not in rec}
     merged.update(rec)
     with open(out_json, "w") as f:
         json.dump(dict(sorted(merged.items())), f, indent=1)
         f.write("\n")
-    _traffic_md(rec, workload, info, fscale, wscale, out_md, command)
+    here = {k: v for k, v in merged.items() if k.endswith(":" + workload)}
+    _traffic_md(here, workload, info, out_md)
     return rec
 
 
-def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
+KERNEL_ORDER = ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
+                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "recursive_chained_kernel")
+
+
+def _traffic_md(rec, workload, info, out_md):
+    """The Markdown summary of every record of one workload, with the
+    commands of the passes that produced them and each pass's calibration."""
     what = {"rs_direct_kernel": "ReduceScatter, direct", "ag_direct_kernel": "AllGather, direct",
             "ar_direct_kernel": "AllReduce, direct (one kernel)",
             "ring_step_kernel": "AllReduce, stepwise ring (all steps)",
@@ -173,29 +188,35 @@ def _traffic_md(rec, workload, info, fscale, wscale, out_md, command):
             "ring_chained_kernel": "AllReduce, chained ring (one launch)",
             "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)",
             "recursive_chained_kernel": "AllReduce, chained recursive halving + doubling (one launch)"}
+    order = {k: i for i, k in enumerate(KERNEL_ORDER)}
+    keys = sorted(rec, key=lambda k: order.get(k.split(":")[0], len(order)))
+    commands = []
+    for k in keys:
+        for c in rec[k].get("pass_commands", []) + [rec[k]["command"]]:
+            if c not in commands:
+                commands.append(c)
+    scales = sorted({(round(1 / r["fetch_scale"], 4), round(1 / r["write_scale"], 6)) for r in rec.values()})
     lines = [
         f"# HBM traffic of the library's kernels (rocprofv3 counters), {workload}",
         "",
         "Commands (from `/tmp` with `TMPDIR=/tmp`; `<repo>` is the repository root):",
         "",
         "```",
-        f"rocprofv3 --pmc FETCH_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py "
-        f"--workload {workload} --counters-pass",
-        f"rocprofv3 --pmc WRITE_SIZE --kernel-trace -d <out> -o pmc --output-format csv -- python <repo>/bench.py "
-        f"--workload {workload} --counters-pass",
-        command,
+        *commands,
         "```",
         "",
-        f"Calibration: the same pass runs `ccl_sim_pad_identity` with nothing to pad, a plain copy that reads and "
-        f"writes exactly {info['copy_read_bytes']:,} bytes. FETCH_SIZE reports {1 / fscale:.4f} of the bytes read "
-        f"and WRITE_SIZE {1 / wscale:.6f} of the bytes written; every kernel's counters are multiplied by those "
-        f"factors. Figures are per call, summed over the call's dispatches.",
+        f"Calibration: every pass runs `ccl_sim_pad_identity` with nothing to pad, a plain copy that reads and "
+        f"writes exactly {info['copy_read_bytes']:,} bytes, and each kernel's counters are multiplied by the factors "
+        f"that copy gives in the same pass. FETCH_SIZE / WRITE_SIZE reported "
+        + "; ".join(f"{f} / {w}" for f, w in scales) +
+        " of the copy's bytes. Figures are per call, summed over the call's dispatches.",
         "",
         "| call | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B | traffic B "
         "| algorithmic B | traffic / algorithmic | source digest |",
         "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---|",
     ]
-    for key, r in rec.items():
+    for key in keys:
+        r = rec[key]
         kernel = key.split(":")[0]
         lines.append(
             f"| {what.get(kernel, kernel)} | `{kernel}` | {r['dispatches']} | {r['fetch_size_kib']:.1f} | "
