@@ -93,36 +93,72 @@ __device__ inline void ag_tile(const ShardArgs& a, int s, uint64_t seg, uint64_t
 // 5.8 -> 6.15 TB/s at M = 2^28 float32, 7 % faster in bf16, 5-8 % at
 // M = 2^24 and 2^26, 3 % at N = 16, even at N = 4, and 18 % slower at
 // N = 2, where each half stores a single copy; with H = 4 it fell to
-// 4.7 TB/s at N = 8.  The tile is the 256-lane tile of AgPolicy, so both
-// kernels share the grid and the ragged-tile bounds.
+// 4.7 TB/s at N = 8.  A part is 256 lanes of one vector each by default
+// (CCL_SIM_AG_PART_LANES, CCL_SIM_AG_PART_VECS); 512-lane parts measured
+// within 1 % at N = 8 to 32 except +6 % in bf16 at N = 8, two vectors per
+// lane 6-11 % slower.
+#ifndef CCL_SIM_AG_PART_LANES
+#define CCL_SIM_AG_PART_LANES 256
+#endif
+#ifndef CCL_SIM_AG_PART_VECS
+#define CCL_SIM_AG_PART_VECS 1
+#endif
+#ifndef CCL_SIM_AG_PART_ROTATE_MAX
+#define CCL_SIM_AG_PART_ROTATE_MAX 6
+#endif
+using AgPartPolicy = Policy<CCL_SIM_AG_PART_LANES, CCL_SIM_AG_PART_VECS, true, kStoreWriteThrough>;
+
+// The i-th output part h of H stores.  Part h stores outputs h·N/H ..
+// (h+1)·N/H - 1.  When a part has at most CCL_SIM_AG_PART_ROTATE_MAX of
+// them, the part on tile `seg` of its shard starts at output seg mod count
+// and wraps, so that the parts in flight at one moment store into
+// different outputs.  Measured with two parts, side by side against the
+// unrotated order on the same buffers (float32 unless noted): N = 4 +7 %,
+// N = 6 +9 %, N = 8 +3.5 % (AllGather 1.605 against 1.661 ms at M = 2^28;
+// the bench step's RS + AG 3.152 against 3.234 ms; bf16 +6 %; M = 2^24
+// +10 %, M = 2^26 +5.5 %), N = 12 +2 %; at N = 16 and 24 within 1 %, and
+// at N = 32 4 % slower and bf16 at N = 16 3.5 % slower, so larger parts
+// keep the plain order.  Two other orders were measured and not kept:
+// outputs interleaved between the parts (h, h + H, ...: -2 to +9 %) and the
+// odd parts walking theirs backwards (+3.5 % at N = 8 float32, -1 % bf16).
+__device__ inline int part_output(int h, int H, int i, int nranks, int* count, uint64_t seg) {
+  const int k0 = h * nranks / H, k1 = (h + 1) * nranks / H;
+  *count = k1 - k0;
+  if (*count > 0 && *count <= CCL_SIM_AG_PART_ROTATE_MAX) return k0 + int((uint64_t(i) + seg) % uint64_t(*count));
+  return k0 + i;
+}
+
 template <class T, int H>
 __device__ inline void ag_tile_parts(const ShardArgs& a, int s, uint64_t seg, uint64_t len) {
+  using P = AgPartPolicy;
   constexpr int V = vec_elems<T>();
-  constexpr uint64_t kTile = tile_of<AgPolicy>(V);
-  static_assert(AgPolicy::TB == 256 && AgPolicy::U == 1, "a part is one 256-lane, one-vector tile");
+  constexpr uint64_t kTile = tile_of<P>(V);
   using S = typename T::S;
   using SV = typename VecOf<S, V>::type;
-  const int h = static_cast<int>(threadIdx.x) / 256, l = static_cast<int>(threadIdx.x) % 256;
+  const int h = static_cast<int>(threadIdx.x) / P::TB, l = static_cast<int>(threadIdx.x) % P::TB;
   const uint64_t base = uint64_t(s) * a.q;
   const uint64_t t0 = seg * kTile;
   const S* src = in_ptr<T>(a.send, s) + t0;
   if (t0 + kTile <= len) {
-    const SV v = vload<S, V, AgPolicy::NTL>(src + uint64_t(l) * V);
-    const int k0 = h * a.nranks / H, k1 = (h + 1) * a.nranks / H;
-    for (int k = k0; k < k1; ++k)
-      store_through(out_ptr<T>(a.recv, k) + base + t0, uint32_t(kTile * sizeof(S)),
-                    uint32_t(l * V * static_cast<int>(sizeof(S))), v);
+    SV v[P::U];
+#pragma unroll
+    for (int u = 0; u < P::U; ++u) v[u] = vload<S, V, P::NTL>(src + uint64_t(u * P::TB + l) * V);
+    int count = 0;
+    part_output(h, H, 0, a.nranks, &count, seg);
+    for (int i = 0; i < count; ++i) {
+      const int k = part_output(h, H, i, a.nranks, &count, seg);
+#pragma unroll
+      for (int u = 0; u < P::U; ++u)
+        store_through(out_ptr<T>(a.recv, k) + base + t0, uint32_t(kTile * sizeof(S)),
+                      uint32_t((u * P::TB + l) * V * static_cast<int>(sizeof(S))), v[u]);
+    }
     return;
   }
-  // the ragged last tile of a shard: half 0 copies its valid elements
+  // the ragged last tile of a shard: part 0 copies its valid elements
   if (h != 0) return;
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint64_t j = t0 + uint64_t(l) * V + uint64_t(i);
-    if (j < len) {
-      const S x = get1(src + uint64_t(l) * V + uint64_t(i));
-      for (int k = 0; k < a.nranks; ++k) put1(out_ptr<T>(a.recv, k) + base + j, x);
-    }
+  for (uint64_t j = t0 + uint64_t(l); j < len && j < t0 + kTile; j += P::TB) {
+    const S x = get1(src - t0 + j);
+    for (int k = 0; k < a.nranks; ++k) put1(out_ptr<T>(a.recv, k) + base + j, x);
   }
 }
 
@@ -139,7 +175,7 @@ __device__ inline void ag_tile_parts(const ShardArgs& a, int s, uint64_t seg, ui
 // CCL_SIM_AG_PARTS_FROM ranks, and from 64 up, where the rotated fan-out
 // order matters); H > 1: 256·H-lane workgroups split into H parts.
 template <class T, int H>
-__global__ __launch_bounds__(AgPolicy::TB * H) void ag_direct_kernel(ShardArgs a) {
+__global__ __launch_bounds__((H > 1 ? AgPartPolicy::TB : AgPolicy::TB) * H) void ag_direct_kernel(ShardArgs a) {
   constexpr uint64_t kTile = tile_of<AgPolicy>(vec_elems<T>());
   for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int s = rank_of_tile(tile, a.tiles_per_shard);
@@ -355,13 +391,15 @@ hipError_t run_direct(const Call& c) {
           return hipGetLastError();
         }
       }
-      const ShardArgs a = shard_args<AgPolicy, T>(c);
-      const unsigned grid = grid_for(a.ntiles, c.num_cus);
-      if (c.nranks >= CCL_SIM_AG_PARTS_FROM && c.nranks < CCL_SIM_ROTATE_FROM)
-        hipLaunchKernelGGL((ag_direct_kernel<T, CCL_SIM_AG_PARTS>), dim3(grid), dim3(CCL_SIM_AG_PARTS * AgPolicy::TB), 0,
+      if (c.nranks >= CCL_SIM_AG_PARTS_FROM && c.nranks < CCL_SIM_ROTATE_FROM) {
+        const ShardArgs a = shard_args<AgPartPolicy, T>(c);
+        hipLaunchKernelGGL((ag_direct_kernel<T, CCL_SIM_AG_PARTS>), dim3(grid_for(a.ntiles, c.num_cus)),
+                           dim3(CCL_SIM_AG_PARTS * AgPartPolicy::TB), 0, c.stream, a);
+      } else {
+        const ShardArgs a = shard_args<AgPolicy, T>(c);
+        hipLaunchKernelGGL((ag_direct_kernel<T, 1>), dim3(grid_for(a.ntiles, c.num_cus)), dim3(AgPolicy::TB), 0,
                            c.stream, a);
-      else
-        hipLaunchKernelGGL((ag_direct_kernel<T, 1>), dim3(grid), dim3(AgPolicy::TB), 0, c.stream, a);
+      }
       return hipGetLastError();
     }
     const uint64_t produced = (c.coll == kAllReduce) ? c.limit : uint64_t(c.nranks) * c.q;
