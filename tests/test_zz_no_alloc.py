@@ -2,7 +2,8 @@
 ccl_sim_allreduce with a caller-owned workspace, bit for bit, through the C
 ABI: two calls in a row on the same scratch, the second smaller than the
 first, for every schedule the entry point offers, with and without pointer
-tables, in float32, bf16 and int32."""
+tables, in float32, bf16 and int32; and the call captured into a HIP graph
+and replayed, with other calls reusing the scratch between replays."""
 
 import numpy as np
 import pytest
@@ -100,3 +101,47 @@ def test_noalloc_refusals_enqueue_nothing(cs):
     assert all(bool((o == 3.0).all()) for o in out)
     got = np.stack([U.to_host(o, "float32") for o in out])
     assert np.all(got == 3.0)
+
+
+@pytest.mark.parametrize("schedule", ["direct", "ring_stepwise", "ring_chained", "recursive", "recursive_chained"])
+@pytest.mark.parametrize("n,m", [(8, 3 * 8 * 1024 + 5), (128, 128 * 37 - 11)])
+def test_noalloc_graph_replays_match_eager(cs, schedule, n, m):
+    """The call allocates nothing, so it can be captured once its first call
+    on the device has read the scratch's address.  Between replays, eager
+    noalloc calls of another shape reuse the same scratch; every replay must
+    still equal an eager call with a caller-owned workspace, bit for bit."""
+    send = [torch.empty(m, device="cuda") for _ in range(n)]
+    recv = [torch.empty(m, device="cuda") for _ in range(n)]
+    want = [torch.empty(m, device="cuda") for _ in range(n)]
+    other_in = [torch.rand(m // 2 + 1, device="cuda") for _ in range(n)]
+    other_out = [torch.empty(m // 2 + 1, device="cuda") for _ in range(n)]
+    ws = cs.Workspace("allreduce", n, m, "float32", schedule)
+    gen = torch.Generator(device="cuda").manual_seed(n + m)
+
+    def refill():
+        for t in send:
+            t.uniform_(-1, 1, generator=gen)
+
+    refill()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        cs.ccl_sim_allreduce_noalloc(send, recv, m, schedule=schedule)  # first call outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        cs.ccl_sim_allreduce_noalloc(send, recv, m, schedule=schedule)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        refill()
+        for t in recv:
+            t.fill_(float("nan"))
+        cs.ccl_sim_allreduce_noalloc(other_in, other_out, m // 2 + 1, schedule=schedule)  # the scratch reused
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        cs.ccl_sim_allreduce(send, want, m, schedule=schedule, workspace=ws)
+        torch.cuda.synchronize()
+        for r in range(n):
+            assert torch.equal(recv[r].view(torch.int32), want[r].view(torch.int32)), (schedule, replay, r)
