@@ -283,7 +283,7 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
  *
  * Workspace bytes one call needs (0 when none, SIZE_MAX for invalid
  * arguments), each part rounded up to 256 bytes:
- *   - a barrier block of 1152 bytes for the persistent ring;
+ *   - a barrier block of 640 bytes for the persistent ring;
  *   - two pointer tables of 8·N bytes each when nranks > 64;
  *   - the ring's double-buffered partials 2·N·q·a (a = accumulator size: 4
  *     for bf16, else the element size) for ring ReduceScatter and ring
