@@ -185,3 +185,37 @@ def test_label_rows_on_every_row_shape():
     assert bench.row_kernels("rs_ag_direct", "w") == (["rs_direct_kernel", "ag_direct_kernel"], "w")
     assert bench.row_kernels("rs_ag_ring_chained_m2^24", "w") is None
     assert bench.row_kernels("allreduce_direct_8x268435456_bf16", "w") is None
+
+
+def test_traffic_merges_passes_over_different_schedules(tmp_path):
+    """The persistent ring's counters come from a pass of their own: a
+    second pass on the same workload replaces only the kernels it measured,
+    keeps the first pass's records, and the summary lists every record of
+    the workload with both passes' commands."""
+    header = ["Kernel_Name", "Counter_Value"]
+    ring = "void ccl::(anonymous namespace)::ring_step_kernel<ccl::F32, 0, Policy<256, 1, true, 2>>(RingArgs)"
+    pers = "void ccl::(anonymous namespace)::ring_persistent_kernel<ccl::F32, 0, Policy<256, 4, true, 2>, false>(R)"
+    out, md = tmp_path / "t.json", tmp_path / "t.md"
+
+    def one_pass(name, kernel_name, kernel, schedules_arg):
+        _write_csv(tmp_path / f"{name}.f.csv", header, [[PAD, 512.0], [AG, 64.0], [kernel_name, 1536.0]])
+        _write_csv(tmp_path / f"{name}.w.csv", header, [[PAD, 1024.0], [AG, 1024.0], [kernel_name, 2048.0]])
+        info = {"counters_pass": True, "copy_read_bytes": 1 << 20, "copy_write_bytes": 1 << 20,
+                "counters_schedules_arg": schedules_arg,
+                "calls": {"ag_direct_kernel": 9 * 128 * 1024, kernel: 5 * 1024 * 1024},
+                "kernel_source_digests": {"ag_direct_kernel": "a" * 16, kernel: "d" * 16, "pad_kernel": "c" * 16}}
+        (tmp_path / f"{name}.out").write_text(json.dumps(info) + "\n")
+        return profiling.traffic(str(tmp_path / f"{name}.f.csv"), str(tmp_path / f"{name}.w.csv"),
+                                 str(tmp_path / f"{name}.out"), "w", str(out), str(md), f"cmd {name}")
+
+    one_pass("rest", ring, "ring_step_kernel", "direct,ring_stepwise")
+    one_pass("pers", pers, "ring_persistent_kernel", "ring_persistent")
+    merged = json.loads(out.read_text())
+    assert set(merged) == {"ag_direct_kernel:w", "ring_step_kernel:w", "ring_persistent_kernel:w"}
+    assert merged["ring_step_kernel:w"]["command"] == "cmd rest"
+    assert merged["ring_persistent_kernel:w"]["command"] == "cmd pers"
+    assert merged["ring_persistent_kernel:w"]["traffic_over_algorithmic"] == pytest.approx(1.0)
+    text = md.read_text()
+    assert "`ring_step_kernel`" in text and "`ring_persistent_kernel`" in text and "`ag_direct_kernel`" in text
+    assert "--counters-schedules direct,ring_stepwise" in text and "--counters-schedules ring_persistent" in text
+    assert text.index("`ag_direct_kernel`") < text.index("`ring_step_kernel`") < text.index("`ring_persistent_kernel`")
