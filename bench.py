@@ -492,13 +492,33 @@ def collective_context(cs, coll, nranks, payload_bytes, seconds):
             "modeled_ring_ib_hdr_ms": ring["time_s"] * 1e3}
 
 
+def pacer_cycles(torch, stream, target_ms=1.0):
+    """Argument of torch.cuda._sleep for a GPU spin of about target_ms on
+    this device (the spin counts clock ticks whose rate is measured here)."""
+    probe = 1_000_000
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(probe)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = max(a.elapsed_time(b), 1e-3)
+    return int(min(max(probe * target_ms / ms, 1e4), 2e9))
+
+
 def time_interleaved(torch, stream, cases, iters, context=None):
     """Time every case with HIP events on `stream`: one warm-up call each,
     then `iters` rounds that run every case once, in forward order in even
     rounds and reverse order in odd ones, so that no case always follows the
-    same neighbour.  A case that raises is reported, not fatal.  `context`
+    same neighbour.  Each round starts with a GPU spin of about 1 ms: the
+    rounds are separated by a device synchronisation, and without the spin
+    the round's first case would start on an idle GPU and count the host's
+    work for its call (marshalling 2N tensor addresses: about 190 us at
+    N = 256) as GPU time, while every later case's host work overlaps the
+    case before it.  A case that raises is reported, not fatal.  `context`
     maps a case name to (coll, nranks, payload bytes) for the nccl-tests
     style figures of collective_context."""
+    spin = pacer_cycles(torch, stream)
     res, live = {}, []
     for name, fn, nbytes in cases:
         try:
@@ -512,6 +532,7 @@ def time_interleaved(torch, stream, cases, iters, context=None):
     for rnd in range(iters):
         order = live if rnd % 2 == 0 else live[::-1]
         ev = []
+        torch.cuda._sleep(spin)
         for name, fn, _ in order:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
