@@ -411,7 +411,7 @@ def ccl_sim_recursive_route(nranks, phase, step, rank):
 
 def ccl_sim_persistent_aborted(workspace):
     """True if the last persistent-ring call that used `workspace` stopped
-    at its barrier's poll limit (its outputs are then incomplete).  Call it
+    at a wait's poll limit (its outputs are then incomplete).  Call it
     once that call's stream work has completed, and before another call
     reuses the workspace (the other schedules keep their partials where the
     persistent ring's control block was)."""

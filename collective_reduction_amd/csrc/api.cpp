@@ -14,6 +14,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "ccl_sim.h"
 #include "internal.hpp"
@@ -130,19 +131,32 @@ constexpr int kMaxPersistentPerCu = 4;
 //                                        limit
 //   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU, 1..4
 //                                        (anything else is refused before a launch)
-//   CCL_SIM_SPIN_LIMIT=n                 persistent ring barrier poll limit
+//   CCL_SIM_PERSISTENT_SYNC=grid|flags   persistent ring step ordering: a grid
+//                                        barrier, or per-workgroup step flags;
+//                                        unset, empty or "auto": by step size
+//                                        (anything else is refused before a launch)
+//   CCL_SIM_SPIN_LIMIT=n                 persistent ring poll limit
 struct Env {
   bool debug = false;
   int per_cu = 0;
+  int sync = kSyncAuto;  // -1: not a known value
+  const char* sync_text = "";
   unsigned spin_limit = 0;
   Env() {
     if (const char* v = std::getenv("CCL_SIM_DEBUG")) debug = std::atoi(v) != 0;
     if (const char* v = std::getenv("CCL_SIM_PERSISTENT_BLOCKS_PER_CU")) per_cu = std::atoi(v);
+    if (const char* v = std::getenv("CCL_SIM_PERSISTENT_SYNC")) {
+      sync_text = v;
+      sync = (v[0] == '\0' || std::strcmp(v, "auto") == 0) ? kSyncAuto
+             : std::strcmp(v, "grid") == 0                   ? kSyncGrid
+             : std::strcmp(v, "flags") == 0                  ? kSyncFlags
+                                                             : -1;
+    }
     if (const char* v = std::getenv("CCL_SIM_SPIN_LIMIT")) spin_limit = static_cast<unsigned>(std::strtoul(v, nullptr, 10));
   }
 };
 
-// Three getenv lookups per call, so that a process can change a knob
+// Four getenv lookups per call, so that a process can change a knob
 // between calls.
 Env env() { return Env(); }
 
@@ -233,6 +247,9 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
                 "CCL_SIM_PERSISTENT_BLOCKS_PER_CU=%d: the persistent ring runs 1 to %d workgroups per CU (0 = the "
                 "default); larger grids are not known to be co-resident",
                 knobs.per_cu, kMaxPersistentPerCu);
+  if (effective_schedule(nranks, schedule) == CCL_SIM_RING_PERSISTENT && knobs.sync < 0)
+    return fail(CCL_SIM_INVALID_ARGUMENT, "CCL_SIM_PERSISTENT_SYNC=\"%.64s\": expected grid, flags or auto",
+                knobs.sync_text);
   const size_t es = elem_size(dtype);
 
   // Counts ([DECOMP] §源码一 count rules; §Contract 实验四 capacity check).
@@ -320,6 +337,7 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   if (lay.ctrl != SIZE_MAX) c.ctrl = reinterpret_cast<unsigned*>(ws + lay.ctrl);
   c.stream = stream;
   c.persistent_per_cu = knobs.per_cu;
+  c.persistent_sync = knobs.sync;
   c.spin_limit = knobs.spin_limit;
   c.log_plan = knobs.debug;
 
@@ -370,19 +388,20 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     if (c.log_plan)
       std::fprintf(stderr,
                    "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu lanes=%d "
-                   "tiles/step=%llu coherent=%d\n",
+                   "tiles/step=%llu coherent=%d sync=%s\n",
                    coll, nranks, static_cast<unsigned long long>(q), c.num_cus, plan.occupancy_per_cu, plan.per_cu,
                    static_cast<unsigned long long>(plan.grid), plan.lanes,
-                   static_cast<unsigned long long>(plan.tiles_per_step), plan.coherent ? 1 : 0);
+                   static_cast<unsigned long long>(plan.tiles_per_step), plan.coherent ? 1 : 0,
+                   plan.flags ? "flags" : "grid");
     if (e == hipSuccess && c.log_plan) {
-      // Debug check of the barrier's watchdog: wait for the kernel and read
-      // the abort word it raises when a barrier runs into the poll limit.
+      // Debug check of the watchdog: wait for the kernel and read the abort
+      // word it raises when a barrier or flag wait runs into the poll limit.
       unsigned abort_word = 0;
       e = hipStreamSynchronize(stream);
       if (e == hipSuccess)
         e = hipMemcpy(&abort_word, c.ctrl + kCtrlAbort, sizeof(abort_word), hipMemcpyDeviceToHost);
       if (e == hipSuccess && abort_word != 0)
-        return fail(CCL_SIM_HIP_ERROR, "persistent ring barrier reached its poll limit; the results are incomplete");
+        return fail(CCL_SIM_HIP_ERROR, "persistent ring wait reached its poll limit; the results are incomplete");
     }
   }
   if (e != hipSuccess) return fail(CCL_SIM_HIP_ERROR, "kernel launch failed: %s", hipGetErrorString(e));

@@ -22,12 +22,14 @@ struct Call {
   bool in_place = false;   // AllGather: sendbufs[r] == recvbufs[r] + r·sendcount for every r
   RankPtrs send{}, recv{};
   void* partial = nullptr; // ring partials [2][nranks][q], or recursive-halving scratch [nranks][nranks/2·q]
-  unsigned* ctrl = nullptr;// persistent ring: barrier counter and abort flag
+  unsigned* ctrl = nullptr;// persistent ring: barrier counters, abort word and step flags
   hipStream_t stream = nullptr;
   int num_cus = 0;
-  // Persistent ring: workgroups per compute unit (0 = the default), the
-  // barrier's poll limit, and whether to log the launch plan to stderr.
+  // Persistent ring: workgroups per compute unit (0 = the default), how
+  // its steps are ordered (PersistSync), the poll limit of its waits, and
+  // whether to log the launch plan to stderr.
   int persistent_per_cu = 0;
+  int persistent_sync = 0;
   unsigned spin_limit = 0;
   bool log_plan = false;
 };
@@ -40,8 +42,15 @@ struct PersistentPlan {
   uint64_t tiles_per_step = 0;
   int lanes = 0;  // threads per workgroup
   hipError_t refused = hipSuccess;  // the cooperative launch's error when the runtime refused it
-  bool coherent = false;            // agent-coherent data path, barrier without cache maintenance
+  bool coherent = false;            // agent-coherent data path, waits without cache maintenance
+  bool flags = false;               // steps ordered by per-workgroup flags, not a grid barrier
 };
+
+// How the persistent ring orders its steps: by the library's choice from
+// the step size, by a grid barrier between steps, or by per-workgroup step
+// flags (each workgroup waits only for the workgroups whose data its next
+// step reads).
+enum PersistSync : int { kSyncAuto = 0, kSyncGrid = 1, kSyncFlags = 2 };
 
 // Barrier groups of the persistent ring's two-level arrival.  Measured
 // side by side at N = 256 (256 workgroups): 4 groups 1-1.5 % faster than 8
@@ -53,14 +62,18 @@ struct PersistentPlan {
 
 // Control block of the persistent ring (unsigned words): line 0 holds the
 // global arrival counter and the abort word, line 1 + g the arrival counter
-// of barrier group g; a line is 128 bytes.
+// of barrier group g (a line is 128 bytes), and from kCtrlFlags on one step
+// flag per workgroup of the flag-ordered form, which launches at most
+// kCtrlMaxFlags workgroups (4 per CU on a 1024-CU device).
 enum CtrlWord : int {
   kCtrlBarrier = 0,
   kCtrlAbort = 1,
   kCtrlLine = 32,
   kCtrlGroups = CCL_SIM_CTRL_GROUPS,
   kCtrlGroup = kCtrlLine,
-  kCtrlWords = kCtrlLine * (1 + kCtrlGroups),
+  kCtrlFlags = kCtrlLine * (1 + kCtrlGroups),
+  kCtrlMaxFlags = 4096,
+  kCtrlWords = kCtrlFlags + kCtrlMaxFlags,
 };
 
 hipError_t run_direct(const Call& c);

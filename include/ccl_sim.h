@@ -43,8 +43,9 @@
  *            256-byte aligned, owned by the caller.  It carries the device
  *            copy of the pointer tables when nranks > 64, the partial sums
  *            the ring schedules pass between ranks, the per-rank halves of
- *            the recursive halving schedule, and the barrier block (arrival
- *            counters and an abort word) of the persistent ring.  Calls
+ *            the recursive halving schedule, and the control block (arrival
+ *            counters, step flags and an abort word) of the persistent
+ *            ring.  Calls
  *            that share a workspace must be ordered on one stream.  NULL is
  *            allowed when the required size is 0.
  * Errors.    Every argument is validated before any HIP call; on any error
@@ -136,12 +137,23 @@ typedef enum {
   CCL_SIM_DIRECT = 0,
   /* The ring of [RING] §1 / [PRIMS] §五: one kernel launch per ring step. */
   CCL_SIM_RING_STEPWISE = 1,
-  /* The same ring steps inside one cooperative kernel, a grid-wide barrier
-   * between steps.  CCL_SIM_UNSUPPORTED when the device cannot keep the
-   * grid resident, or when the runtime refuses the cooperative launch (ROCm
-   * does, for instance, while another process on the same GPU holds its
-   * cooperative launch resources); the other schedules are unaffected.
-   * The grid is one workgroup per CU unless the environment variable
+  /* The same ring steps inside one cooperative kernel.  Steps are ordered
+   * in one of two ways, with the same transfers, combining order and
+   * results:
+   *   - a grid-wide barrier between steps;
+   *   - per-workgroup step flags: before a step, each workgroup waits only
+   *     for the workgroups that hold the upstream tiles of its own (the
+   *     chunk it receives from rank r-1), and its partials are keyed by
+   *     chunk as in CCL_SIM_RING_CHAINED.
+   * By default steps of up to 2^25 elements (N·q) take the flags and larger
+   * ones the barrier; the environment variable CCL_SIM_PERSISTENT_SYNC
+   * (grid, flags or auto) overrides this, and any other value makes the
+   * call return CCL_SIM_INVALID_ARGUMENT before anything is enqueued.
+   * CCL_SIM_UNSUPPORTED when the device cannot keep the grid resident, or
+   * when the runtime refuses the cooperative launch (ROCm does, for
+   * instance, while another process on the same GPU holds its cooperative
+   * launch resources); the other schedules are unaffected.  The grid is
+   * one workgroup per CU unless the environment variable
    * CCL_SIM_PERSISTENT_BLOCKS_PER_CU asks for 1 to 4; any other value
    * (negative, or above 4, where co-residency is not established) makes
    * the call return CCL_SIM_UNSUPPORTED before anything is enqueued. */
@@ -283,7 +295,8 @@ ccl_sim_result_t ccl_sim_pad_identity(const void* const* srcs, void* const* dsts
  *
  * Workspace bytes one call needs (0 when none, SIZE_MAX for invalid
  * arguments), each part rounded up to 256 bytes:
- *   - a barrier block of 640 bytes for the persistent ring;
+ *   - a control block of 17,024 bytes for the persistent ring (barrier
+ *     counters, abort word, one step flag per workgroup);
  *   - two pointer tables of 8·N bytes each when nranks > 64;
  *   - the ring's double-buffered partials 2·N·q·a (a = accumulator size: 4
  *     for bf16, else the element size) for ring ReduceScatter and ring
@@ -325,7 +338,7 @@ uint64_t ccl_sim_algorithmic_bytes(ccl_sim_coll_t coll, int nranks, size_t count
  * §源码二; RECURSIVE log2 N per phase (plus the placement of an
  * out-of-place AllGather); persistent ring, chained ring and chained
  * recursive 1.  Not counted: the pointer-table uploads when
- * nranks > 64 and the persistent ring's barrier reset.  N = 1: 1.
+ * nranks > 64 and the persistent ring's control-block reset.  N = 1: 1.
  * Returns -1 for invalid arguments. */
 int ccl_sim_launch_count(ccl_sim_coll_t coll, int nranks, size_t count, ccl_sim_schedule_t schedule,
                          int in_place);
@@ -426,8 +439,9 @@ const char* ccl_sim_result_string(ccl_sim_result_t result);
 
 /*
  * The persistent ring's watchdog (a diagnostic, not an operation of the
- * pages).  Its grid barrier polls a bounded number of times.  A barrier
- * can run into that bound only if the device does not keep the whole
+ * pages).  Its grid barrier and its flag waits poll a bounded number of
+ * times.  A wait can run into that bound only if the device does not keep
+ * the whole
  * cooperative grid resident (for instance while other work holds its
  * compute units); every workgroup then stops, the call's outputs are
  * incomplete, and the kernel raises an abort word in the workspace's

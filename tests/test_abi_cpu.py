@@ -165,10 +165,13 @@ def test_workspace_sizes(cs):
     assert ws("allreduce", 8, 1 << 20, "bfloat16", "ring_stepwise") == 2 * 8 * (1 << 17) * 4
     assert ws("allreduce", 2, 1000, "float32", "ring_stepwise") == 0
     assert ws("all_gather", 8, 1000, "float32", "ring_stepwise") == 0
-    assert ws("all_gather", 8, 1000, "float32", "ring_persistent") == 768
+    # persistent ring: control block of 160 barrier words + 4096 step flags, rounded to 256 bytes
+    ctrl = (4256 * 4 + 255) // 256 * 256
+    assert ctrl == 17152
+    assert ws("all_gather", 8, 1000, "float32", "ring_persistent") == ctrl
     # more than 64 ranks: two pointer tables
     assert ws("allreduce", 256, 1 << 22, "float32", "direct") == 2 * 2048
-    assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == 768 + 4096 + 2 * (1 << 22) * 4
+    assert ws("allreduce", 256, 1 << 22, "float32", "ring_persistent") == ctrl + 4096 + 2 * (1 << 22) * 4
     assert ws("allreduce", 1, 100, "float32", "ring_persistent") == 0
     # chained ring: one partial per chunk, N x q accumulators
     assert ws("allreduce", 8, 1 << 20, "float32", "ring_chained") == 8 * (1 << 17) * 4
