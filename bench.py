@@ -74,6 +74,7 @@ KERNEL_FILES = {
     "ar_direct_kernel": "kernels_direct.hip",
     "ring_step_kernel": "kernels_ring.hip",
     "ring_persistent_kernel": "kernels_ring.hip",
+    "ring_persistent_flags_kernel": "kernels_ring.hip",
     "ring_chained_kernel": "kernels_ring.hip",
     "recursive_step_kernel": "kernels_recursive.hip",
     "recursive_chained_kernel": "kernels_recursive.hip",
@@ -124,22 +125,55 @@ AR_KERNEL = {"direct": "ar_direct_kernel", "ring_stepwise": "ring_step_kernel",
              "ring_persistent": "ring_persistent_kernel", "ring_chained": "ring_chained_kernel",
              "recursive": "recursive_step_kernel", "recursive_chained": "recursive_chained_kernel"}
 ROW_WORKLOADS = {"256x4194304_fp32": "normal_256x4194304_fp32", "256x6553600_bf16": "normal_256x6553600_bf16"}
+PERSISTENT_KERNEL = {"grid": "ring_persistent_kernel", "flags": "ring_persistent_flags_kernel"}
+
+
+def persistent_ordering(nranks, count):
+    """How the library's persistent ring orders the steps of an AllReduce
+    of this shape ("grid" or "flags"), as the library itself reports it."""
+    from collective_reduction_amd import ccl_sim
+    return ccl_sim.ccl_sim_persistent_ordering("allreduce", nranks, count)
+
+
+def ar_kernel(schedule, nranks, count):
+    """The kernel an AllReduce of `schedule` runs on N = nranks, M = count:
+    the persistent ring's kernel depends on how it orders the steps."""
+    if schedule == "ring_persistent":
+        return PERSISTENT_KERNEL[persistent_ordering(nranks, count)]
+    return AR_KERNEL[schedule]
+
+
+def row_shape(name, default_workload):
+    """(row name without its workload suffix, workload, N, M) of a bench
+    row: the 256-rank rows name their workload, the _m2^k rows run the
+    default workload's first 2^k positions, the rest the default workload;
+    N and M are None for a workload this module does not know."""
+    from collective_reduction_amd import inputs as I
+    workload = default_workload
+    for suffix, wl in ROW_WORKLOADS.items():
+        if name.endswith("_" + suffix):
+            name, workload = name[:-len(suffix) - 1], wl
+            break
+    spec = I.WORKLOADS.get(workload)
+    n, m = (spec["nranks"], spec["count"]) if spec else (None, None)
+    if "_m2^" in name:
+        name, lg = name.rsplit("_m2^", 1)
+        m = 1 << int(lg)
+    return name, workload, n, m
 
 
 def row_kernels(name, default_workload):
     """(kernels, workload) whose committed counters cover one bench row, or
     None: the AllReduce rows (one kernel each), the direct ReduceScatter
     alone, and the direct RS+AG pair."""
-    workload = default_workload
-    for suffix, wl in ROW_WORKLOADS.items():
-        if name.endswith("_" + suffix):
-            name, workload = name[:-len(suffix) - 1], wl
-            break
-    else:
-        if "_m2^" in name or name.endswith("_bf16"):
-            return None
+    if "_m2^" in name or (name.endswith("_bf16") and not any(name.endswith("_" + s) for s in ROW_WORKLOADS)):
+        return None
+    name, workload, n, m = row_shape(name, default_workload)
     if name.startswith("allreduce_") and name[len("allreduce_"):] in AR_KERNEL:
-        return [AR_KERNEL[name[len("allreduce_"):]]], workload
+        schedule = name[len("allreduce_"):]
+        if schedule == "ring_persistent" and n is None:
+            return None
+        return [ar_kernel(schedule, n, m)], workload
     if name == "rs_only_direct":
         return ["rs_direct_kernel"], workload
     if name == "rs_ag_direct":
@@ -169,6 +203,10 @@ def label_rows(rows, default_workload):
         if row.get("gbs") is not None:
             cached = "chained" in name or "cache_resident" in name
             row["rate_kind"] = "effective_cache_assisted" if cached else "hbm"
+        if "ring_persistent" in name:
+            _, _, n, m = row_shape(name, default_workload)
+            if n is not None:
+                row["ordering"] = persistent_ordering(n, m)
         cover = row_kernels(name, default_workload)
         if cover is None:
             continue
@@ -462,9 +500,10 @@ def counters_pass(cs, torch, stream, send, shards, recv, n, m, q, dtype, schedul
     cs.ccl_sim_pad_identity(send, recv, m, m, "sum", stream=stream)
     calls = {"rs_direct_kernel": cs.ccl_sim_algorithmic_bytes("reduce_scatter", n, m, dtype, "direct"),
              "ag_direct_kernel": cs.ccl_sim_algorithmic_bytes("all_gather", n, m, dtype, "direct")}
-    for schedule, kernel in AR_KERNEL.items():
+    for schedule in AR_KERNEL:
         if schedule not in schedules or (schedule.startswith("recursive") and n & (n - 1)):
             continue
+        kernel = ar_kernel(schedule, n, m)
         ws = cs.Workspace("allreduce", n, m, dtype, schedule)
         cs.ccl_sim_allreduce(send, recv, m, schedule=schedule, workspace=ws, stream=stream)
         torch.cuda.synchronize()

@@ -96,6 +96,7 @@ _recursive_route = _sig("ccl_sim_recursive_route", ctypes.c_int,
                          ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)])
 _result_string = _sig("ccl_sim_result_string", ctypes.c_char_p, [ctypes.c_int])
 _persistent_aborted = _sig("ccl_sim_persistent_aborted", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)])
+_persistent_ordering = _sig("ccl_sim_persistent_ordering", ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_size])
 _last_error = _sig("ccl_sim_last_error", ctypes.c_char_p, [])
 _version = _sig("ccl_sim_version", ctypes.c_int, [])
 
@@ -122,7 +123,7 @@ EXPORTED = ("ccl_sim_reduce_scatter", "ccl_sim_all_gather", "ccl_sim_allreduce",
             "ccl_sim_workspace_size", "ccl_sim_algorithmic_bytes", "ccl_sim_launch_count", "ccl_sim_ring_owner",
             "ccl_sim_ring_route", "ccl_sim_result_string", "ccl_sim_last_error", "ccl_sim_version",
             "ccl_sim_model_estimate", "ccl_sim_busbw_factor", "ccl_sim_recursive_route",
-            "ccl_sim_persistent_aborted", "ccl_sim_allreduce_noalloc")
+            "ccl_sim_persistent_aborted", "ccl_sim_allreduce_noalloc", "ccl_sim_persistent_ordering")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CCL_SIM_NOALLOC_SCRATCH_BYTES
 
 
@@ -419,6 +420,17 @@ def ccl_sim_persistent_aborted(workspace):
     flag = ctypes.c_int()
     _check(_persistent_aborted(wp, ctypes.byref(flag)))
     return bool(flag.value)
+
+
+def ccl_sim_persistent_ordering(coll, nranks, count):
+    """How a persistent-ring call of these arguments orders its steps under
+    the current environment: "grid" (a grid barrier between steps) or
+    "flags" (per-workgroup step flags); None when the call runs no ring
+    (nranks 1, count 0).  `count` is M, as for ccl_sim_workspace_size."""
+    v = _persistent_ordering(_enum(COLLS, coll, "coll"), nranks, count)
+    if v < 0:
+        raise CclSimError(INVALID_ARGUMENT, "invalid arguments or CCL_SIM_PERSISTENT_SYNC value")
+    return {0: None, 1: "grid", 2: "flags"}[v]
 
 
 def ccl_sim_result_string(code):

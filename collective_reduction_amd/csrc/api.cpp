@@ -641,6 +641,15 @@ const char* ccl_sim_result_string(ccl_sim_result_t result) {
 
 const char* ccl_sim_last_error(void) { return g_last_error; }
 
+int ccl_sim_persistent_ordering(ccl_sim_coll_t coll, int nranks, size_t count) {
+  if (!valid_coll(coll) || nranks < 1 || nranks > CCL_SIM_MAX_RANKS) return -1;
+  const Env knobs = env();
+  if (knobs.sync < 0) return -1;
+  if (count == 0 || effective_schedule(nranks, CCL_SIM_RING_PERSISTENT) != CCL_SIM_RING_PERSISTENT) return 0;
+  return persistent_uses_flags(nranks, shard_len(count, nranks), knobs.sync) ? CCL_SIM_ORDER_FLAGS
+                                                                             : CCL_SIM_ORDER_GRID;
+}
+
 ccl_sim_result_t ccl_sim_persistent_aborted(const void* workspace, int* aborted) {
   clear_error();
   if (workspace == nullptr || aborted == nullptr)

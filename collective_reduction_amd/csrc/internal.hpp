@@ -80,6 +80,9 @@ hipError_t run_direct(const Call& c);
 hipError_t run_ring_stepwise(const Call& c);
 // Sets *unsupported when no co-resident grid can be formed.
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan);
+// Whether the persistent ring orders a call's steps by flags (else by the
+// grid barrier): `sync` is the caller's PersistSync, q the chunk length.
+bool persistent_uses_flags(int nranks, uint64_t q, int sync);
 hipError_t run_recursive(const Call& c);
 hipError_t run_ring_chained(const Call& c);
 hipError_t run_recursive_chained(const Call& c);

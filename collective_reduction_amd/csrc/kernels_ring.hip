@@ -654,6 +654,10 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
 #define CCL_SIM_PERSIST_FLAGS_STEP CCL_SIM_PERSIST_COHERENT_STEP
 #endif
 
+bool persistent_uses_flags(int nranks, uint64_t q, int sync) {
+  return sync == kSyncFlags || (sync == kSyncAuto && uint64_t(nranks) * q <= CCL_SIM_PERSIST_FLAGS_STEP);
+}
+
 hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan* plan) {
   *unsupported = false;
   return by_type(c.dtype, [&]<class T>() -> hipError_t {
@@ -661,8 +665,7 @@ hipError_t run_ring_persistent(const Call& c, bool* unsupported, PersistentPlan*
     const uint64_t step = uint64_t(c.nranks) * c.q;
     const bool small = step <= CCL_SIM_PERSIST_SMALL_STEP;
     const bool coherent = step <= CCL_SIM_PERSIST_COHERENT_STEP;
-    const bool flags = c.persistent_sync == kSyncFlags ||
-                       (c.persistent_sync == kSyncAuto && step <= CCL_SIM_PERSIST_FLAGS_STEP);
+    const bool flags = persistent_uses_flags(c.nranks, c.q, c.persistent_sync);
     return by_op<T>(op, [&]<class U, int OP>() -> hipError_t {
       if (flags)
         return small ? launch_persistent<U, OP, PersistSmallPolicy, true, true>(c, unsupported, plan)

@@ -31,8 +31,8 @@ import sys
 
 def _short(name):
     for key in ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
-                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "recursive_chained_kernel",
-                "pad_kernel", "reset_ctrl_kernel",
+                "ring_persistent_kernel", "ring_persistent_flags_kernel", "ring_chained_kernel",
+                "recursive_step_kernel", "recursive_chained_kernel", "pad_kernel", "reset_ctrl_kernel",
                 "store_table_kernel"):
         if key in name:
             return key
@@ -175,7 +175,8 @@ def traffic(fetch_csv, write_csv, pass_out, workload, out_json, out_md, command)
 
 
 KERNEL_ORDER = ("rs_direct_kernel", "ag_direct_kernel", "ar_direct_kernel", "ring_step_kernel",
-                "ring_persistent_kernel", "ring_chained_kernel", "recursive_step_kernel", "recursive_chained_kernel")
+                "ring_persistent_kernel", "ring_persistent_flags_kernel", "ring_chained_kernel",
+                "recursive_step_kernel", "recursive_chained_kernel")
 
 
 def _traffic_md(rec, workload, info, out_md):
@@ -184,7 +185,8 @@ def _traffic_md(rec, workload, info, out_md):
     what = {"rs_direct_kernel": "ReduceScatter, direct", "ag_direct_kernel": "AllGather, direct",
             "ar_direct_kernel": "AllReduce, direct (one kernel)",
             "ring_step_kernel": "AllReduce, stepwise ring (all steps)",
-            "ring_persistent_kernel": "AllReduce, persistent ring (one launch)",
+            "ring_persistent_kernel": "AllReduce, persistent ring, grid barrier (one launch)",
+            "ring_persistent_flags_kernel": "AllReduce, persistent ring, step flags (one launch)",
             "ring_chained_kernel": "AllReduce, chained ring (one launch)",
             "recursive_step_kernel": "AllReduce, recursive halving + doubling (all steps)",
             "recursive_chained_kernel": "AllReduce, chained recursive halving + doubling (one launch)"}

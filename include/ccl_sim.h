@@ -463,6 +463,19 @@ const char* ccl_sim_result_string(ccl_sim_result_t result);
  */
 ccl_sim_result_t ccl_sim_persistent_aborted(const void* workspace, int* aborted);
 
+/*
+ * How a CCL_SIM_RING_PERSISTENT call orders its steps (a diagnostic, not an
+ * operation of the pages): CCL_SIM_ORDER_GRID, a grid barrier between
+ * steps, or CCL_SIM_ORDER_FLAGS, per-workgroup step flags.  `count` is M,
+ * the logical per-rank length, as for ccl_sim_workspace_size; the answer
+ * depends on N·ceil(M/N) and on CCL_SIM_PERSISTENT_SYNC, read now.  0 when
+ * the call would run no ring (nranks 1, count 0); -1 for invalid arguments
+ * or an unknown CCL_SIM_PERSISTENT_SYNC value.  No HIP call is made.
+ */
+#define CCL_SIM_ORDER_GRID 1
+#define CCL_SIM_ORDER_FLAGS 2
+int ccl_sim_persistent_ordering(ccl_sim_coll_t coll, int nranks, size_t count);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char* ccl_sim_last_error(void);
 

@@ -341,6 +341,62 @@ def test_persistent_grid_request_is_capped(cs, monkeypatch):
     assert got != cs.UNSUPPORTED
 
 
+def test_unknown_step_ordering_is_refused_before_any_hip_call(cs, monkeypatch):
+    """CCL_SIM_PERSISTENT_SYNC other than grid, flags, auto or empty makes a
+    persistent-ring call fail with CCL_SIM_INVALID_ARGUMENT before anything
+    is enqueued; the other schedules do not read it."""
+    n, m = 4, 1000
+    s, r = fake(n, m, 4), fake(n, m, 4, base=BASE * 3)
+    need = cs.ccl_sim_workspace_size("allreduce", n, m, "float32", "ring_persistent")
+    ws = (BASE * 7, need)
+    ar = cs.ccl_sim_allreduce
+    for bad in ("barrier", "GRID", "1"):
+        monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", bad)
+        assert code_of(ar, s, r, m, dtype="float32", schedule="ring_persistent", workspace=ws) == cs.INVALID_ARGUMENT
+        assert "CCL_SIM_PERSISTENT_SYNC" in cs.ccl_sim_last_error()
+        got = code_of(ar, s, r, m, dtype="float32", schedule="ring_stepwise", workspace=ws)
+        assert got != cs.INVALID_ARGUMENT or "CCL_SIM_PERSISTENT_SYNC" not in cs.ccl_sim_last_error()
+    for good in ("grid", "flags", "auto", ""):
+        monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", good)
+        code_of(ar, s, r, m, dtype="float32", schedule="ring_persistent", workspace=ws)
+        assert "CCL_SIM_PERSISTENT_SYNC" not in cs.ccl_sim_last_error()
+
+
+def test_persistent_ordering_query(cs, monkeypatch):
+    """The persistent ring takes per-workgroup step flags for steps (N chunks
+    of ceil(M/N)) of up to 2^25 elements and the grid barrier above, unless
+    CCL_SIM_PERSISTENT_SYNC says otherwise; the query answers without a GPU."""
+    monkeypatch.delenv("CCL_SIM_PERSISTENT_SYNC", raising=False)
+    po = cs.ccl_sim_persistent_ordering
+    assert po("allreduce", 256, 1 << 22) == "flags"
+    assert po("allreduce", 256, 6_553_600) == "flags"
+    assert po("reduce_scatter", 8, 1 << 24) == "flags"
+    assert po("allreduce", 8, 1 << 25) == "flags"            # a step of exactly 2^25
+    assert po("allreduce", 8, (1 << 25) + 1) == "grid"       # q rounds up: a step of 2^25 + 8
+    assert po("allreduce", 3, (1 << 25) - 1) == "grid"       # 3 x 11,184,811 = 2^25 + 1
+    assert po("all_gather", 8, 1 << 26) == "grid"
+    assert po("allreduce", 8, 1 << 28) == "grid"
+    assert po("allreduce", 1, 1 << 20) is None               # one rank: the direct copy
+    assert po("allreduce", 8, 0) is None
+    monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", "grid")
+    assert po("allreduce", 256, 1 << 22) == "grid"
+    monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", "flags")
+    assert po("allreduce", 8, 1 << 28) == "flags"
+    monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", "auto")
+    assert po("allreduce", 8, 1 << 28) == "grid"
+    monkeypatch.setenv("CCL_SIM_PERSISTENT_SYNC", "sometimes")
+    with pytest.raises(cs.CclSimError):
+        po("allreduce", 8, 1 << 20)
+    monkeypatch.delenv("CCL_SIM_PERSISTENT_SYNC")
+    lib = cs._lib
+    lib.ccl_sim_persistent_ordering.restype = ctypes.c_int
+    lib.ccl_sim_persistent_ordering.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
+    assert lib.ccl_sim_persistent_ordering(7, 8, 1000) == -1   # not a collective
+    assert lib.ccl_sim_persistent_ordering(2, 0, 1000) == -1
+    assert lib.ccl_sim_persistent_ordering(2, 1025, 1000) == -1  # above CCL_SIM_MAX_RANKS
+    assert lib.ccl_sim_persistent_ordering(2, 256, 1 << 22) == 2  # CCL_SIM_ORDER_FLAGS
+
+
 def test_noalloc_allreduce_limits_are_checked_before_any_hip_call(cs):
     """ccl_sim_allreduce_noalloc refuses the persistent ring and any call
     whose workspace would not fit the library's scratch before touching the

@@ -158,7 +158,8 @@ def test_label_rows_on_every_row_shape():
     """Timed rows get a CV flag and a rate kind; the chained drivers and
     the cache-resident shape are labelled cache-assisted; rows with a list
     of CVs (the latency ratio) or without a rate are left as they are;
-    rows covered by counters get their traffic ratio."""
+    rows covered by counters get their traffic ratio; the persistent-ring
+    rows say how their steps were ordered."""
     rows = {
         "allreduce_ring_stepwise": {"gbs": 5000.0, "cv": 0.01},
         "rs_ag_direct": {"gbs": 6000.0, "cv": 0.07},
@@ -167,6 +168,9 @@ def test_label_rows_on_every_row_shape():
         "ratio_rs_ag_over_allreduce_direct": {"of": "a / b", "ratio": None, "cv": [0.01, 0.09]},
         "launch_floor_allreduce_direct_8x64": {"gbs": None, "calls": 100},
         "rs_ag_ring_chained_m2^24": {"gbs": 7000.0, "cv": 0.02},
+        "allreduce_ring_persistent": {"gbs": 5600.0, "cv": 0.01},
+        "rs_ag_ring_persistent_m2^24": {"gbs": 6000.0, "cv": 0.01},
+        "allreduce_ring_persistent_256x6553600_bf16": {"gbs": 5600.0, "cv": 0.01},
         "broken": {"error": "refused"},
         "ratio_missing": None,
     }
@@ -179,9 +183,17 @@ def test_label_rows_on_every_row_shape():
     assert rows["rs_ag_direct_8x1048576_fp32_cache_resident"]["rate_kind"] == "effective_cache_assisted"
     assert "cv_over_5pct" not in rows["ratio_rs_ag_over_allreduce_direct"]
     assert rows["broken"] == {"error": "refused"}
+    # the persistent rows say how the library ordered their steps
+    assert rows["allreduce_ring_persistent"]["ordering"] == "grid"
+    assert rows["rs_ag_ring_persistent_m2^24"]["ordering"] == "flags"
+    assert rows["allreduce_ring_persistent_256x6553600_bf16"]["ordering"] == "flags"
+    assert "ordering" not in rows["allreduce_ring_stepwise"]
     assert "rate_kind" not in rows["launch_floor_allreduce_direct_8x64"]
     assert bench.row_kernels("allreduce_ring_persistent_256x6553600_bf16", "w") == \
-        (["ring_persistent_kernel"], "normal_256x6553600_bf16")
+        (["ring_persistent_flags_kernel"], "normal_256x6553600_bf16")
+    assert bench.row_kernels("allreduce_ring_persistent", "uniform_8x268435456_fp32") == \
+        (["ring_persistent_kernel"], "uniform_8x268435456_fp32")
+    assert bench.row_kernels("allreduce_ring_persistent", "w") is None
     assert bench.row_kernels("rs_ag_direct", "w") == (["rs_direct_kernel", "ag_direct_kernel"], "w")
     assert bench.row_kernels("rs_ag_ring_chained_m2^24", "w") is None
     assert bench.row_kernels("allreduce_direct_8x268435456_bf16", "w") is None
