@@ -118,12 +118,18 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
 // CO: agent-coherent data accesses (the persistent ring, whose waits then
 // need no cache maintenance; see load_vec_coherent).
 //
-// ring_body_at takes the tile as (rank r, tile seg of the chunk), which the
-// persistent kernels compute once per call for a workgroup's first tile.
-template <class T, int OP, class P, bool CO = false>
-__device__ inline void ring_body_at(const RingArgs& a, int step, int r, uint64_t seg) {
+// AT: the tile is given as (rank r_at, tile seg_at of the chunk), which the
+// flag-ordered persistent kernel computes once per call for a workgroup's
+// first tile; otherwise it is found from `tile`.  (One body for both: a
+// separate function for the (rank, segment) form measured 3 % slower in
+// the fenced persistent kernel at N = 8, M = 2^28, where the compiler then
+// waited for every store of a tile before starting the next.)
+template <class T, int OP, class P, bool CO = false, bool AT = false>
+__device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile, int r_at = 0, uint64_t seg_at = 0) {
   constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   const int n = a.nranks;
+  const int r = AT ? r_at : rank_of_tile(tile, a.tiles_per_chunk);
+  const uint64_t seg = AT ? seg_at : tile - uint64_t(r) * a.tiles_per_chunk;
   int c;
   bool reduce = false;
   const typename T::S* src;
@@ -161,12 +167,6 @@ __device__ inline void ring_body_at(const RingArgs& a, int step, int r, uint64_t
     else
       copy_tile<T, P, false, CO>(src, dst, seg, len);
   }
-}
-
-template <class T, int OP, class P, bool CO = false>
-__device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile) {
-  const int r = rank_of_tile(tile, a.tiles_per_chunk);
-  ring_body_at<T, OP, P, CO>(a, step, r, tile - uint64_t(r) * a.tiles_per_chunk);
 }
 
 template <class T, int OP, class P>
@@ -322,8 +322,6 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
   constexpr bool kAhead = CCL_SIM_PERSIST_AHEAD && sizeof(typename T::A) == sizeof(typename T::S);
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
-  const int r0 = rank_of_tile(blockIdx.x, a.tiles_per_chunk);  // the first tile, blockIdx.x < ntiles
-  const uint64_t seg0 = blockIdx.x - uint64_t(r0) * a.tiles_per_chunk;
   unsigned epoch = 0;
   typename LF::SV ahead[P::U];
   for (int step = a.first_step; step < nsteps; ++step) {
@@ -331,8 +329,9 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
     RsTileAt first;
     if (step > a.first_step) {
       grid_arrive<CO>(a.ctrl, epoch + 1);
-      if (kAhead && a.coll != kAllGather && step < n - 1) {
-        first = rs_tile_at<P, T>(a, step, r0, seg0);
+      if (kAhead && a.coll != kAllGather && step < n - 1 && uint64_t(blockIdx.x) < a.ntiles) {
+        const int r = rank_of_tile(blockIdx.x, a.tiles_per_chunk);
+        first = rs_tile_at<P, T>(a, step, r, blockIdx.x - uint64_t(r) * a.tiles_per_chunk);
         if (first.full) {
           const LF ln(first.seg, first.len);
           const typename T::S* mine = in_ptr<T>(a.send, first.r) + uint64_t(first.c) * a.q;
@@ -343,12 +342,12 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
       }
       if (!grid_wait<CO>(a.ctrl, ++epoch, a.spin_limit)) return;
     }
-    if (have_ahead)
-      ring_rs_tile<T, OP, P, true, CO>(a, step, first.r, first.seg, first.c, first.len, ahead);
-    else
-      ring_body_at<T, OP, P, CO>(a, step, r0, seg0);
-    for (uint64_t tile = blockIdx.x + gridDim.x; tile < a.ntiles; tile += gridDim.x)
-      ring_body<T, OP, P, CO>(a, step, tile);
+    for (uint64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+      if (have_ahead && tile == blockIdx.x)
+        ring_rs_tile<T, OP, P, true, CO>(a, step, first.r, first.seg, first.c, first.len, ahead);
+      else
+        ring_body<T, OP, P, CO>(a, step, tile);
+    }
   }
 }
 
@@ -451,7 +450,7 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a
   if (threadIdx.x == 0) s_bad = 0;  // seen by every wave after the first step's flags_publish
   for (int step = a.first_step; step < nsteps; ++step) {
     if (step > a.first_step && !flags_wait(a, step, up, whole_grid, &s_bad)) return;
-    ring_body_at<T, OP, P, true>(a, step, r0, seg0);
+    ring_body<T, OP, P, true, true>(a, step, 0, r0, seg0);
     for (uint64_t tile = blockIdx.x + gridDim.x; tile < a.ntiles; tile += gridDim.x)
       ring_body<T, OP, P, true>(a, step, tile);
     flags_publish(a, step);
