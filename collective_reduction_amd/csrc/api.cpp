@@ -127,8 +127,8 @@ constexpr int kMaxPersistentPerCu = 4;
 //                                        a ring or recursive call, so a read of a
 //                                        partial before its write shows in the
 //                                        result; after a persistent ring, wait for
-//                                        it and report a barrier that hit its poll
-//                                        limit
+//                                        it and report a barrier or flag wait that
+//                                        hit its poll limit
 //   CCL_SIM_PERSISTENT_BLOCKS_PER_CU=k   persistent ring workgroups per CU, 1..4
 //                                        (anything else is refused before a launch)
 //   CCL_SIM_PERSISTENT_SYNC=grid|flags   persistent ring step ordering: a grid

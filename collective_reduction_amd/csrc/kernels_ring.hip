@@ -1,6 +1,6 @@
 // Ring schedule: one launch per step, one persistent cooperative kernel
-// with a grid barrier between steps, or each chunk's steps chained in one
-// launch.
+// whose steps are ordered by a grid barrier or by per-workgroup step flags,
+// or each chunk's steps chained in one launch.
 
 #include "kernel_common.hpp"
 
@@ -302,8 +302,9 @@ __device__ inline RsTileAt rs_tile_at(const RingArgs& a, int step, int r, uint64
 #endif
 
 // CO: the data path is agent-coherent and the barrier does no cache
-// maintenance (chosen for small steps, where the barrier dominates; see
-// run_ring_persistent).
+// maintenance (for small steps, where the barrier dominates, when the
+// caller asks for the barrier there; by default small steps take the step
+// flags below; see run_ring_persistent).
 //
 // The barrier is split into its arrival and its wait.  In between, a
 // workgroup whose next step is a ReduceScatter step loads the rank's own
