@@ -57,6 +57,7 @@ int log2i(int n) {
 bool valid_coll(int c) { return c >= CCL_SIM_COLL_REDUCE_SCATTER && c <= CCL_SIM_COLL_ALLREDUCE; }
 
 constexpr size_t kAlign = 256;
+constexpr uint64_t kLine = 128;  // bytes in a cache line
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -338,6 +339,9 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
   c.stream = stream;
   c.persistent_per_cu = knobs.per_cu;
   c.persistent_sync = knobs.sync;
+  c.line_aligned = (q * es) % kLine == 0 && (q * accum_size(dtype)) % kLine == 0;
+  for (int r = 0; r < nranks && c.line_aligned; ++r)
+    c.line_aligned = ins[r].lo % kLine == 0 && outs[r].lo % kLine == 0;
   c.spin_limit = knobs.spin_limit;
   c.log_plan = knobs.debug;
 

@@ -30,6 +30,11 @@ struct Call {
   // whether to log the launch plan to stderr.
   int persistent_per_cu = 0;
   int persistent_sync = 0;
+  // Every rank buffer starts on a 128-byte line and a chunk (q elements,
+  // and q accumulators) is a whole number of lines, so no line holds data
+  // of two chunks (the flag-ordered persistent ring reads from an L2 only
+  // then).
+  bool line_aligned = false;
   unsigned spin_limit = 0;
   bool log_plan = false;
 };

@@ -193,7 +193,17 @@ __device__ inline void store_through(void* tile_base, uint32_t tile_bytes, uint3
 // invalidation, only the arrival counters.  The accesses go through a
 // buffer resource over the workgroup's tile (only buffer instructions take
 // explicit cache bits); element accesses cover the ragged ends.
+//
+// Data written earlier in the kernel by a workgroup on the same XCD can
+// instead be read with ordinary loads from that XCD's L2, which every CU of
+// the XCD shares and which the writer's write-through stores updated on
+// their way to memory, provided the reader's CU first drops its own L1
+// (buffer_inv sc0).  Whether a load may do so is the caller's to decide
+// (the flag-ordered persistent ring compares the writer's XCD with its own
+// at run time).  Side by side, loads with sc0 instead of ordinary ones ran
+// as slowly as agent-scope loads.
 constexpr int kAgentScope = 16;  // sc1
+constexpr int kStreamLoad = 2;   // nt: an ordinary load with the nontemporal hint
 using W4 = unsigned __attribute__((ext_vector_type(4)));
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* tile_base, uint32_t tile_bytes) {
   const uint64_t addr = reinterpret_cast<uint64_t>(tile_base);
@@ -201,17 +211,17 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* tile_base, uint32
   const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32))));
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), 0, int(tile_bytes), kRsrcWord3);
 }
-template <class EV>
+template <class EV, int BITS = kAgentScope>
 __device__ inline EV load_vec_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   if constexpr (sizeof(EV) == 16) {
-    return __builtin_bit_cast(EV, __builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, kAgentScope));
+    return __builtin_bit_cast(EV, __builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, BITS));
   } else {
     static_assert(sizeof(EV) == 32, "one or two 128-bit vectors");
     struct Pair {
       W4 lo, hi;
     };
-    const Pair p{__builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, kAgentScope),
-                 __builtin_amdgcn_raw_buffer_load_b128(rs, int(off) + 16, 0, kAgentScope)};
+    const Pair p{__builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, BITS),
+                 __builtin_amdgcn_raw_buffer_load_b128(rs, int(off) + 16, 0, BITS)};
     return __builtin_bit_cast(EV, p);
   }
 }
@@ -229,14 +239,14 @@ __device__ inline void store_vec_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t of
     __builtin_amdgcn_raw_buffer_store_b128(p.hi, rs, int(off) + 16, 0, kSystemScope);
   }
 }
-template <class E>
+template <class E, int BITS = kAgentScope>
 __device__ inline E load1_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   if constexpr (sizeof(E) == 2)
-    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(rs, int(off), 0, kAgentScope));
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b16(rs, int(off), 0, BITS));
   else if constexpr (sizeof(E) == 4)
-    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, int(off), 0, kAgentScope));
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b32(rs, int(off), 0, BITS));
   else
-    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, int(off), 0, kAgentScope));
+    return __builtin_bit_cast(E, __builtin_amdgcn_raw_buffer_load_b64(rs, int(off), 0, BITS));
 }
 template <class E>
 __device__ inline void store1_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t off, E v) {
@@ -259,8 +269,14 @@ __device__ inline int lane_count(uint64_t j, uint64_t len, int v) {
 // the valid range, so every vector is complete and no lane checks a count;
 // otherwise each vector carries its count of valid elements (0..V) and
 // incomplete ones move element by element.
-template <class T, class P, bool FULL, bool CO = false>
+//
+// XCD (with CO): loads are ordinary ones with the nontemporal hint, through
+// the L1 and the XCD's L2, for data that the caller knows to be fresh there;
+// they keep the buffer form, whose base sits in scalar registers; stores
+// are the same.
+template <class T, class P, bool FULL, bool CO = false, bool XCD = false>
 struct Lane {
+  static constexpr int kLoadBits = XCD ? kStreamLoad : kAgentScope;
   using S = typename T::S;
   using A = typename T::A;
   static constexpr int U = P::U;
@@ -301,11 +317,11 @@ struct Lane {
     if constexpr (CO) {
       const auto rs = rsrc(base);
       const uint32_t off = offset<E>(u);
-      if (whole(u)) return load_vec_coherent<EV>(rs, off);
+      if (whole(u)) return load_vec_coherent<EV, kLoadBits>(rs, off);
       EV v = {};
 #pragma unroll
       for (int k = 0; k < V; ++k)
-        if (k < cnt[u]) v[k] = load1_coherent<E>(rs, off + uint32_t(k * int(sizeof(E))));
+        if (k < cnt[u]) v[k] = load1_coherent<E, kLoadBits>(rs, off + uint32_t(k * int(sizeof(E))));
       return v;
     }
     if (whole(u)) return vload<E, V, P::NTL>(base + j[u]);
@@ -370,8 +386,8 @@ struct Lane {
         if constexpr (CO) {
           const auto rs = tile_rsrc(base + t0, uint32_t(tv * sizeof(A)));
           const uint32_t off = uint32_t((u * P::TB + static_cast<int>(threadIdx.x)) * int(sizeof(H)));
-          lo = load_vec_coherent<H>(rs, off);
-          hi = load_vec_coherent<H>(rs, off + uint32_t(tv / 2 * sizeof(A)));
+          lo = load_vec_coherent<H, kLoadBits>(rs, off);
+          hi = load_vec_coherent<H, kLoadBits>(rs, off + uint32_t(tv / 2 * sizeof(A)));
         } else {
           const A* half0 = base + t0 + uint64_t(u * P::TB + static_cast<int>(threadIdx.x)) * (V / 2);
           lo = vload<A, V / 2, P::NTL>(half0);
@@ -468,9 +484,9 @@ __device__ inline SV finish_vec(const typename T::A (&acc)[vec_elems<T>()], int 
 
 // Copy of `len` elements from src to dst for one tile (AllGather steps and
 // the stand-alone AllGather's own-shard placement).
-template <class T, class P, bool FULL, bool CO = false>
+template <class T, class P, bool FULL, bool CO = false, bool XCD = false>
 __device__ inline void copy_tile(const typename T::S* src, typename T::S* dst, uint64_t seg, uint64_t len) {
-  using L = Lane<T, P, FULL, CO>;
+  using L = Lane<T, P, FULL, CO, XCD>;
   const L ln(seg, len);
   typename L::SV v[P::U];
 #pragma unroll

@@ -37,6 +37,8 @@ struct RingArgs {
   int chunk_keyed;           // partials keyed by chunk (chained ring) instead of [step parity][rank]
   unsigned* ctrl;
   unsigned spin_limit;
+  int xcd_map;               // flag-ordered persistent ring: ring neighbours placed on one XCD
+  int xcd_loads;             // flag-ordered persistent ring: L2 reads allowed (no line spans two chunks)
 };
 
 __device__ inline int mod_n(int x, int n) {
@@ -58,11 +60,11 @@ __device__ inline uint64_t chunk_len(const RingArgs& a, int c) {
 // out_r[chunk c] (the AllGather phase's source: the phase boundary fused
 // in one state machine as in [DECOMP] §源码三), ReduceScatter into
 // recvbufs[c], c = r+1.
-template <class T, int OP, class P, bool FULL, bool CO>
+template <class T, int OP, class P, bool FULL, bool CO, bool XCD = false>
 __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t seg, int c, uint64_t len,
-                                    const typename Lane<T, P, FULL, CO>::SV* own_ahead = nullptr) {
+                                    const typename Lane<T, P, FULL, CO, XCD>::SV* own_ahead = nullptr) {
   using A = typename T::A;
-  using L = Lane<T, P, FULL, CO>;
+  using L = Lane<T, P, FULL, CO, XCD>;
   constexpr int V = vec_elems<T>();
   const int n = a.nranks;
   const int up = mod_n(r - 1, n);
@@ -124,7 +126,7 @@ __device__ inline void ring_rs_tile(const RingArgs& a, int t, int r, uint64_t se
 // separate function for the (rank, segment) form measured 3 % slower in
 // the fenced persistent kernel at N = 8, M = 2^28, where the compiler then
 // waited for every store of a tile before starting the next.)
-template <class T, int OP, class P, bool CO = false, bool AT = false>
+template <class T, int OP, class P, bool CO = false, bool AT = false, bool XCD = false>
 __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile, int r_at = 0, uint64_t seg_at = 0) {
   constexpr uint64_t kTile = tile_of<P>(vec_elems<T>());
   const int n = a.nranks;
@@ -157,15 +159,15 @@ __device__ inline void ring_body(const RingArgs& a, int step, uint64_t tile, int
   const bool full = (seg + 1) * kTile <= len;
   if (reduce) {
     if (full)
-      ring_rs_tile<T, OP, P, true, CO>(a, step, r, seg, c, len);
+      ring_rs_tile<T, OP, P, true, CO, XCD>(a, step, r, seg, c, len);
     else
-      ring_rs_tile<T, OP, P, false, CO>(a, step, r, seg, c, len);
+      ring_rs_tile<T, OP, P, false, CO, XCD>(a, step, r, seg, c, len);
   } else {
     typename T::S* dst = out_ptr<T>(a.recv, r) + uint64_t(c) * a.q;
     if (full)
-      copy_tile<T, P, true, CO>(src, dst, seg, len);
+      copy_tile<T, P, true, CO, XCD>(src, dst, seg, len);
     else
-      copy_tile<T, P, false, CO>(src, dst, seg, len);
+      copy_tile<T, P, false, CO, XCD>(src, dst, seg, len);
   }
 }
 
@@ -374,43 +376,71 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
 // flag, and the loads of data written by other workgroups are agent-scope
 // (sc1) loads issued after the wait, so no cache maintenance is needed.
 //
-// A workgroup's tiles are b, b + G, ... (G = gridDim.x).  The workgroups
-// it waits on do not change from step to step, so they are found once per
-// call: with up to 64 tiles per step, lane i of wave 0 keeps the index of
-// the workgroup holding the upstream tile of the i-th tile
-// (flags_upstream) and waits on it.  With more tiles per step (only steps
-// far larger than the flags are chosen for by default) lane i waits on
-// workgroups i, i + 64, ... instead, that is on the whole grid: a superset
-// of the dependencies, which keeps the wait to one short loop.
+// Placement.  Workgroup b holds the tiles f(b), f(b) + G, f(b) + 2G, ...
+// (G = gridDim.x), where f is the identity, or, with xcd_map, the
+// permutation f(b) = (b mod 8)·G/8 + b/8 of [0, G).  Workgroups are spread
+// over the eight XCDs in turn (workgroup b on XCD b mod 8), so with xcd_map
+// the tiles of one eighth of [0, G) share an XCD, and a tile and its
+// upstream tile (r-1, seg), tiles_per_chunk before it, share one unless
+// they straddle an eighth.  The host sets xcd_map where that places more
+// neighbours together than the identity does.  Only speed depends on it: the
+// kernel compares XCDs at run time (below) before it reads from an L2.
+__device__ inline uint64_t first_tile(const RingArgs& a, uint64_t b) {
+  const uint64_t g = gridDim.x;
+  return a.xcd_map ? (b % 8) * (g / 8) + b / 8 : b;
+}
+__device__ inline uint64_t holder_of(const RingArgs& a, uint64_t t) {
+  const uint64_t g = gridDim.x, m = t % g;
+  return a.xcd_map ? (m % (g / 8)) * 8 + m / (g / 8) : m;
+}
 __device__ inline uint64_t tiles_of_block(const RingArgs& a) {
-  const uint64_t g = gridDim.x, b = blockIdx.x;
-  return b < a.ntiles ? (a.ntiles - b + g - 1) / g : 0;
+  const uint64_t g = gridDim.x, f = first_tile(a, blockIdx.x);
+  return f < a.ntiles ? (a.ntiles - f + g - 1) / g : 0;
 }
 
-// The lane's first flag: a workgroup index, or -1 for none (a tile whose
-// upstream tile is the workgroup's own, whose steps before are done).
+// The workgroups a workgroup waits on do not change from step to step, so
+// they are found once per call: with up to 64 tiles per step, lane i of
+// wave 0 keeps the index of the workgroup holding the upstream tile of the
+// i-th tile and waits on it.  With more tiles per step (only steps far
+// larger than the flags are chosen for by default) lane i waits on
+// workgroups i, i + 64, ... instead, that is on the whole grid: a superset
+// of the dependencies, which keeps the wait to one short loop.
+//
+// The lane's first flag: a workgroup index, or -1 for none (no i-th tile, or
+// a tile whose upstream tile is the workgroup's own, whose steps before are
+// done).
 __device__ inline int flags_upstream(const RingArgs& a, bool whole_grid) {
   if (threadIdx.x >= 64) return -1;
   if (whole_grid) return int(threadIdx.x) < int(gridDim.x) ? int(threadIdx.x) : -1;
   if (threadIdx.x >= tiles_of_block(a)) return -1;
-  const uint64_t g = gridDim.x, b = blockIdx.x;
-  const uint64_t t = b + threadIdx.x * g;
+  const uint64_t t = first_tile(a, blockIdx.x) + uint64_t(threadIdx.x) * gridDim.x;
   const uint64_t back = a.tiles_per_chunk;  // tile (r-1, seg) is tile - tiles_per_chunk, modulo ntiles
-  const uint64_t w = (t >= back ? t - back : t + a.ntiles - back) % g;
-  return w == b ? -1 : static_cast<int>(w);
+  const uint64_t w = holder_of(a, t >= back ? t - back : t + a.ntiles - back);
+  return w == blockIdx.x ? -1 : static_cast<int>(w);
 }
+
+// A flag word holds the steps its workgroup has completed in its low 24
+// bits and the workgroup's XCD in its top 8.
+constexpr unsigned kFlagSteps = 0xFFFFFFu;
+__device__ inline unsigned xcd_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)); }
 
 // Waits until the flags reach `step`; false once the poll limit is reached
 // or another workgroup has raised the abort word.  `bad` is
 // workgroup-shared, 0 until a wait fails; the workgroup then stops.
-__device__ inline bool flags_wait(const RingArgs& a, int step, int first, bool whole_grid, int* bad) {
+// `local` (workgroup-shared) gets bit i set when the i-th tile's upstream
+// workgroup runs on this workgroup's XCD (or is this workgroup), read from
+// the XCD field of the flag it waited on; never in the whole-grid form.
+__device__ inline bool flags_wait(const RingArgs& a, int step, int first, bool whole_grid, unsigned xcd, int* bad,
+                                  uint64_t* local) {
   if (threadIdx.x < 64) {
     unsigned spins = 0;
-    bool ok = true;
+    bool ok = true, near = !whole_grid;
     for (int w = first; ok && w >= 0 && w < int(gridDim.x); w = whole_grid ? w + 64 : -1) {
       if (w == int(blockIdx.x)) continue;
       const unsigned* flag = a.ctrl + kCtrlFlags + w;
-      while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < unsigned(step)) {
+      unsigned v;
+      while (((v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & kFlagSteps) <
+             unsigned(step)) {
         if (++spins > a.spin_limit ||
             ((spins & 63u) == 0u &&
              __hip_atomic_load(a.ctrl + kCtrlAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
@@ -420,41 +450,116 @@ __device__ inline bool flags_wait(const RingArgs& a, int step, int first, bool w
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      near = near && (v >> 24) == xcd;
     }
+    const uint64_t mask = __ballot(near);
     if (!ok) *bad = 1;
+    if (threadIdx.x == 0) *local = mask;
   }
   __syncthreads();
   return *bad == 0;
 }
 
-__device__ inline void flags_publish(const RingArgs& a, int step) {
+__device__ inline void flags_publish(const RingArgs& a, int step, unsigned xcd) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(a.ctrl + kCtrlFlags + blockIdx.x, unsigned(step + 1), __ATOMIC_RELAXED,
+    __hip_atomic_store(a.ctrl + kCtrlFlags + blockIdx.x, unsigned(step + 1) | (xcd << 24), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Unlike the grid-barrier form, this one does not load the rank's own
-// input before its wait: the waits are short, and side by side the
-// prefetch was neutral or up to 1 % slower (N = 256, M = 2^22 float32:
-// 3.69 against 3.65 ms).
+// Loads.  Data that another workgroup wrote earlier in the kernel (the
+// incoming partial, the forwarded chunk) is read with agent scope (sc1),
+// or, when the writer runs on the same XCD, with ordinary loads from that
+// XCD's L2, after this CU's L1 is dropped (buffer_inv sc0): the writer's
+// write-through stores completed (vmcnt 0) before it published the flag
+// this workgroup waited on, and they passed through that same L2, which
+// they update.  A tile's other reads, the rank's own input and the first
+// step's sources, hold data written before the kernel, or by this
+// workgroup (the in-place forms); they take the L2 form too.  The first
+// step waits on nothing and reads only such data.  Side by side at N = 256,
+// M = 2^22 float32: 3.25 against 3.66 ms with agent scope throughout.
+//
+// The L2 form is used only where no cache line holds data of two chunks
+// (xcd_loads: line-aligned rank buffers and chunks).  Otherwise a line at a
+// chunk boundary can be filled into the reader's L2 for the neighbouring
+// chunk while the writer of this chunk's end is storing into it, and the
+// fill can carry the old bytes: measured at N = 16, q = 777 float32, where
+// the last elements of chunks came out stale.  Misaligned calls keep agent
+// scope for every load.
+//
+// The rank's own input for the first tile of a ReduceScatter step is
+// loaded before the wait, as in the grid-barrier form: x^(r) at a position
+// that step reads is written, in the in-place forms, only by later steps of
+// the same chunk's chain.
+#ifndef CCL_SIM_FLAGS_AHEAD
+#define CCL_SIM_FLAGS_AHEAD 1
+#endif
 template <class T, int OP, class P>
 __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a) {
+  using LX = Lane<T, P, true, true, true>;  // the prefetch of own input, from the L2 or with agent scope
+  using LA = Lane<T, P, true, true, false>;
+  constexpr bool kAhead = CCL_SIM_FLAGS_AHEAD && sizeof(typename T::A) == sizeof(typename T::S);
   __shared__ int s_bad;
+  __shared__ uint64_t s_local;
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
+  const unsigned xcd = xcd_id();
   const bool whole_grid = tiles_of_block(a) > 64;
   const int up = flags_upstream(a, whole_grid);
-  const int r0 = rank_of_tile(blockIdx.x, a.tiles_per_chunk);  // the first tile, blockIdx.x < ntiles
-  const uint64_t seg0 = blockIdx.x - uint64_t(r0) * a.tiles_per_chunk;
+  const uint64_t t0 = first_tile(a, blockIdx.x);  // < ntiles: the grid is at most ntiles
+  const int r0 = rank_of_tile(t0, a.tiles_per_chunk);
+  const uint64_t seg0 = t0 - uint64_t(r0) * a.tiles_per_chunk;
   if (threadIdx.x == 0) s_bad = 0;  // seen by every wave after the first step's flags_publish
+  typename LX::SV ahead[P::U];
   for (int step = a.first_step; step < nsteps; ++step) {
-    if (step > a.first_step && !flags_wait(a, step, up, whole_grid, &s_bad)) return;
-    ring_body<T, OP, P, true, true>(a, step, 0, r0, seg0);
-    for (uint64_t tile = blockIdx.x + gridDim.x; tile < a.ntiles; tile += gridDim.x)
-      ring_body<T, OP, P, true>(a, step, tile);
-    flags_publish(a, step);
+    bool have_ahead = false;
+    RsTileAt first;
+    uint64_t local = a.xcd_loads ? ~uint64_t(0) : 0;
+    if (step > a.first_step) {
+      if (kAhead && a.coll != kAllGather && step < n - 1) {
+        first = rs_tile_at<P, T>(a, step, r0, seg0);
+        if (first.full) {
+          const typename T::S* mine = in_ptr<T>(a.send, first.r) + uint64_t(first.c) * a.q;
+          if (a.xcd_loads) {
+            const LX ln(first.seg, first.len);
+#pragma unroll
+            for (int u = 0; u < P::U; ++u) ahead[u] = ln.load(mine, u);
+          } else {
+            const LA ln(first.seg, first.len);
+#pragma unroll
+            for (int u = 0; u < P::U; ++u) ahead[u] = ln.load(mine, u);
+          }
+          have_ahead = true;
+        }
+      }
+      if (!flags_wait(a, step, up, whole_grid, xcd, &s_bad, &s_local)) return;
+      local = a.xcd_loads ? s_local : 0;
+      // Ordinary loads may hit this CU's L1, which can hold a line read at
+      // an earlier step (in the in-place forms a step can read again what
+      // the first step read).  Drop the L1 (this CU's own cache only)
+      // before reading what the wait released from the L2.
+      if (local != 0) asm volatile("buffer_inv sc0" ::: "memory");
+    }
+    if (local & 1) {
+      if (have_ahead)
+        ring_rs_tile<T, OP, P, true, true, true>(a, step, first.r, first.seg, first.c, first.len, ahead);
+      else
+        ring_body<T, OP, P, true, true, true>(a, step, 0, r0, seg0);
+    } else {
+      if (have_ahead)
+        ring_rs_tile<T, OP, P, true, true, false>(a, step, first.r, first.seg, first.c, first.len, ahead);
+      else
+        ring_body<T, OP, P, true, true, false>(a, step, 0, r0, seg0);
+    }
+    int i = 1;
+    for (uint64_t tile = t0 + gridDim.x; tile < a.ntiles; tile += gridDim.x, ++i) {
+      if (i < 64 && ((local >> i) & 1))
+        ring_body<T, OP, P, true, false, true>(a, step, tile);
+      else
+        ring_body<T, OP, P, true>(a, step, tile);
+    }
+    flags_publish(a, step, xcd);
   }
 }
 
@@ -616,6 +721,12 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
   if (grid > a.ntiles) grid = a.ntiles;
   if (FLAGS && grid > uint64_t(kCtrlMaxFlags)) grid = kCtrlMaxFlags;  // one flag word per workgroup
   if (grid == 0) grid = 1;
+  // Placement of the flag-ordered form (first_tile): with tiles_per_chunk a
+  // multiple of 8 the identity already puts a tile and its upstream tile on
+  // one XCD; otherwise the permutation does for most tiles when the two are
+  // less than an eighth of the grid apart.
+  a.xcd_map = FLAGS && grid % 8 == 0 && a.tiles_per_chunk % 8 != 0 && a.tiles_per_chunk < grid / 8 ? 1 : 0;
+  a.xcd_loads = FLAGS && c.line_aligned ? 1 : 0;
   if (plan) {
     plan->occupancy_per_cu = per_cu;
     plan->per_cu = use;

@@ -101,6 +101,14 @@ CASES = [
     (64, 1000, "bfloat16", "min"),
     (100, 31, "int32", "max"),
     (256, 311, "float32", "sum"),
+    # line-aligned chunks, where the flag form reads data written by a
+    # workgroup on its own XCD from that XCD's L2: one tile per chunk with
+    # the ring's neighbours placed on one XCD (N = 256, 64, 16), and eight
+    # tiles per chunk, where a tile and its upstream share an XCD anyway
+    (256, 1024, "float32", "sum"),
+    (64, 4096, "bfloat16", "max"),
+    (16, 3 * 16384, "float32", "sum"),
+    (8, 8 * 16384, "int32", "sum"),
 ]
 
 
@@ -128,7 +136,8 @@ def test_reduce_scatter_matches_stepwise_and_oracle(cs, sync, n, q, dtype, op, i
 
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("n,q,dtype", [(2, 999, "float32"), (3, 5003, "int64"), (8, 16384 + 9, "bfloat16"),
-                                       (64, 1000, "int32"), (256, 257, "float32")])
+                                       (64, 1000, "int32"), (256, 257, "float32"), (256, 1024, "float32"),
+                                       (64, 8192, "bfloat16")])
 def test_all_gather_matches_stepwise_and_oracle(cs, sync, n, q, dtype, in_place):
     shards = U.random_inputs(n, q, dtype, seed=n * 13 + q)
     recvcount = n * q - 5
@@ -140,7 +149,7 @@ def test_all_gather_matches_stepwise_and_oracle(cs, sync, n, q, dtype, in_place)
 
 
 @pytest.mark.parametrize("n,q,dtype", [(64, 1000, "float32"), (256, 311, "bfloat16"), (256, 16384, "float32"),
-                                       (8, 3 * 16384 + 5, "int32")])
+                                       (8, 3 * 16384 + 5, "int32"), (64, 25600, "bfloat16")])
 def test_repeats_on_the_same_buffers(cs, sync, n, q, dtype):
     """New data on the same workspace and outputs, six calls in a row: the
     flags and counters of one call must not leak into the next."""
