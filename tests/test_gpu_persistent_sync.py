@@ -225,3 +225,46 @@ def test_unknown_value_is_refused_before_any_launch(cs):
             os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
         else:
             os.environ["CCL_SIM_PERSISTENT_SYNC"] = saved
+
+
+RANDOM_ALIGNED = int(os.environ.get("CCL_SIM_TEST_ALIGNED_CASES", "60"))
+
+
+def test_random_line_aligned_shapes_match_stepwise(cs):
+    """Seeded random calls whose rank buffers and chunks are whole 128-byte
+    lines, with the step flags forced, so that the flag form reads
+    same-XCD data from the L2 wherever the placement allows: 2 to 256
+    ranks, every collective, dtype and op, in place and out of place,
+    against the stepwise ring bit for bit (CCL_SIM_TEST_ALIGNED_CASES
+    scales the count)."""
+    rng = np.random.default_rng(20261203)
+    saved = os.environ.get("CCL_SIM_PERSISTENT_SYNC")
+    os.environ["CCL_SIM_PERSISTENT_SYNC"] = "flags"
+    try:
+        for case in range(RANDOM_ALIGNED):
+            n = int(rng.choice([2, 3, 4, 8, 12, 16, 24, 32, 64, 100, 128, 256]))
+            dtype = str(rng.choice(["float32", "bfloat16", "int32", "int64"]))
+            op = str(rng.choice(["sum", "max", "min", "prod", "avg"]))
+            line_elems = 128 // {"float32": 4, "bfloat16": 2, "int32": 4, "int64": 8}[dtype]
+            line_elems = max(line_elems, 32)  # bf16 accumulates in float32: 32 floats per line
+            q = line_elems * int(rng.integers(1, max(2, (1 << 24) // (n * n * line_elems))))  # ~16M elements at most
+            coll = str(rng.choice(["allreduce", "reduce_scatter", "all_gather"]))
+            in_place = bool(rng.integers(0, 2))
+            if coll == "all_gather":
+                xs = U.random_inputs(n, q, dtype, seed=case)
+                got, want = run_pair(cs, coll, xs, dtype, "sum", in_place, recvcount=n * q)
+            elif coll == "reduce_scatter":
+                xs = U.random_inputs(n, n * q, dtype, seed=case, op=op)
+                got, want = run_pair(cs, coll, xs, dtype, op, in_place, q=q)
+            else:
+                xs = U.random_inputs(n, n * q, dtype, seed=case, op=op)
+                got, want = run_pair(cs, coll, xs, dtype, op, in_place)
+            for r in range(n):
+                assert dev_equal(got[r], want[r], dtype), f"case {case}: {coll} n={n} q={q} {dtype} {op} " \
+                                                            f"in_place={in_place} rank {r}"
+        print(f"{RANDOM_ALIGNED} line-aligned random calls matched the stepwise ring", flush=True)
+    finally:
+        if saved is None:
+            os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
+        else:
+            os.environ["CCL_SIM_PERSISTENT_SYNC"] = saved
