@@ -760,9 +760,15 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
 
 // A third threshold picks how steps are ordered when the caller leaves it
 // to the library: per-workgroup flags on the agent-coherent path for steps
-// of up to this many elements, the grid barrier above.
+// of up to this many elements, the grid barrier above.  Measured on
+// line-aligned calls (same-XCD reads on), flags against barrier: N = 8,
+// M = 2^25 AllReduce 0.681 against 0.850 ms; M = 2^26 RS + AG 1.448
+// against 1.666 ms and AllReduce 1.336 against 1.567 ms in float32, 0.900
+// against 1.039 ms in bf16.  Above 2^26 the barrier won in float32 (N = 16,
+// M = 2^27: 7.18 against 7.40 ms; N = 8, M = 2^28: 6.53 against 7.00 ms),
+// once a step no longer fits the 256 MB last-level cache.
 #ifndef CCL_SIM_PERSIST_FLAGS_STEP
-#define CCL_SIM_PERSIST_FLAGS_STEP CCL_SIM_PERSIST_COHERENT_STEP
+#define CCL_SIM_PERSIST_FLAGS_STEP CCL_SIM_PERSIST_SMALL_STEP
 #endif
 
 bool persistent_uses_flags(int nranks, uint64_t q, int sync) {

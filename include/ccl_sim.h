@@ -145,7 +145,7 @@ typedef enum {
    *     for the workgroups that hold the upstream tiles of its own (the
    *     chunk it receives from rank r-1), and its partials are keyed by
    *     chunk as in CCL_SIM_RING_CHAINED.
-   * By default steps of up to 2^25 elements (N·q) take the flags and larger
+   * By default steps of up to 2^26 elements (N·q) take the flags and larger
    * ones the barrier; the environment variable CCL_SIM_PERSISTENT_SYNC
    * (grid, flags or auto) overrides this, and any other value makes the
    * call return CCL_SIM_INVALID_ARGUMENT before anything is enqueued.

@@ -92,9 +92,10 @@ int main(void) {
   CHECK(ccl_sim_persistent_aborted(NULL, &aborted) == CCL_SIM_INVALID_ARGUMENT && aborted == -1);
   CHECK(ccl_sim_persistent_aborted(sends[0], NULL) == CCL_SIM_INVALID_ARGUMENT);
   /* the persistent ring's step ordering, with CCL_SIM_PERSISTENT_SYNC unset:
-     step flags for steps (N chunks of ceil(M/N)) of up to 2^25 elements */
+     step flags for steps (N chunks of ceil(M/N)) of up to 2^26 elements */
   CHECK(ccl_sim_persistent_ordering(CCL_SIM_COLL_ALLREDUCE, 256, 1u << 22) == CCL_SIM_ORDER_FLAGS);
   CHECK(ccl_sim_persistent_ordering(CCL_SIM_COLL_ALLREDUCE, 8, (size_t)1 << 28) == CCL_SIM_ORDER_GRID);
+  CHECK(ccl_sim_persistent_ordering(CCL_SIM_COLL_ALLREDUCE, 8, (size_t)1 << 26) == CCL_SIM_ORDER_FLAGS);
   CHECK(ccl_sim_persistent_ordering(CCL_SIM_COLL_ALLREDUCE, 1, 1000) == 0);
   CHECK(ccl_sim_persistent_ordering((ccl_sim_coll_t)7, 8, 1000) == -1);
 

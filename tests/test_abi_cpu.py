@@ -365,17 +365,19 @@ def test_unknown_step_ordering_is_refused_before_any_hip_call(cs, monkeypatch):
 
 def test_persistent_ordering_query(cs, monkeypatch):
     """The persistent ring takes per-workgroup step flags for steps (N chunks
-    of ceil(M/N)) of up to 2^25 elements and the grid barrier above, unless
+    of ceil(M/N)) of up to 2^26 elements and the grid barrier above, unless
     CCL_SIM_PERSISTENT_SYNC says otherwise; the query answers without a GPU."""
     monkeypatch.delenv("CCL_SIM_PERSISTENT_SYNC", raising=False)
     po = cs.ccl_sim_persistent_ordering
     assert po("allreduce", 256, 1 << 22) == "flags"
     assert po("allreduce", 256, 6_553_600) == "flags"
     assert po("reduce_scatter", 8, 1 << 24) == "flags"
-    assert po("allreduce", 8, 1 << 25) == "flags"            # a step of exactly 2^25
-    assert po("allreduce", 8, (1 << 25) + 1) == "grid"       # q rounds up: a step of 2^25 + 8
-    assert po("allreduce", 3, (1 << 25) - 1) == "grid"       # 3 x 11,184,811 = 2^25 + 1
-    assert po("all_gather", 8, 1 << 26) == "grid"
+    assert po("allreduce", 8, 1 << 25) == "flags"
+    assert po("allreduce", 8, 1 << 26) == "flags"            # a step of exactly 2^26
+    assert po("allreduce", 8, (1 << 26) + 1) == "grid"       # q rounds up: a step of 2^26 + 8
+    assert po("allreduce", 3, 1 << 26) == "grid"             # 3 x 22,369,622 = 2^26 + 2
+    assert po("allreduce", 3, (1 << 26) - 1) == "flags"      # 3 x 22,369,621 = 2^26 - 1
+    assert po("all_gather", 16, 1 << 27) == "grid"
     assert po("allreduce", 8, 1 << 28) == "grid"
     assert po("allreduce", 1, 1 << 20) is None               # one rank: the direct copy
     assert po("allreduce", 8, 0) is None
