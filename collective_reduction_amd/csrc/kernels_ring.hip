@@ -39,6 +39,9 @@ struct RingArgs {
   unsigned spin_limit;
   int xcd_map;               // flag-ordered persistent ring: ring neighbours placed on one XCD
   int xcd_loads;             // flag-ordered persistent ring: L2 reads allowed (no line spans two chunks)
+  // Flag-ordered persistent ring, modulo the grid size G: G - T mod G
+  // (T = tiles_per_chunk), (ntiles - T) mod G and ntiles mod G.
+  unsigned up_back, up_wrap, ntiles_mod;
 };
 
 __device__ inline int mod_n(int x, int n) {
@@ -389,34 +392,42 @@ __device__ inline uint64_t first_tile(const RingArgs& a, uint64_t b) {
   const uint64_t g = gridDim.x;
   return a.xcd_map ? (b % 8) * (g / 8) + b / 8 : b;
 }
-__device__ inline uint64_t holder_of(const RingArgs& a, uint64_t t) {
-  const uint64_t g = gridDim.x, m = t % g;
-  return a.xcd_map ? (m % (g / 8)) * 8 + m / (g / 8) : m;
-}
-__device__ inline uint64_t tiles_of_block(const RingArgs& a) {
-  const uint64_t g = gridDim.x, f = first_tile(a, blockIdx.x);
-  return f < a.ntiles ? (a.ntiles - f + g - 1) / g : 0;
-}
 
-// The workgroups a workgroup waits on do not change from step to step, so
-// they are found once per call: with up to 64 tiles per step, lane i of
-// wave 0 keeps the index of the workgroup holding the upstream tile of the
-// i-th tile and waits on it.  With more tiles per step (only steps far
-// larger than the flags are chosen for by default) lane i waits on
-// workgroups i, i + 64, ... instead, that is on the whole grid: a superset
-// of the dependencies, which keeps the wait to one short loop.
+// The workgroups a workgroup waits on.  Workgroup b takes tiles f, f + G,
+// f + 2G, ... (f = first_tile(b), G workgroups).  The upstream tile of tile
+// t, (r-1, seg), is t - T (T tiles per chunk), or t - T + ntiles for rank
+// 0's tiles (t < T), and which workgroup holds a tile depends only on its
+// index modulo G.  So b's tiles from T on all have their upstream tiles on
+// one workgroup, the holder of f - T (mod G), and its tiles below T (its
+// first ones) on one other, the holder of f - T + ntiles (mod G): at most
+// two workgroups, whatever the number of tiles per step.  Lane 0 of wave 0
+// waits on the first, lane 1 on the second.
 //
-// The lane's first flag: a workgroup index, or -1 for none (no i-th tile, or
-// a tile whose upstream tile is the workgroup's own, whose steps before are
-// done).
-__device__ inline int flags_upstream(const RingArgs& a, bool whole_grid) {
-  if (threadIdx.x >= 64) return -1;
-  if (whole_grid) return int(threadIdx.x) < int(gridDim.x) ? int(threadIdx.x) : -1;
-  if (threadIdx.x >= tiles_of_block(a)) return -1;
-  const uint64_t t = first_tile(a, blockIdx.x) + uint64_t(threadIdx.x) * gridDim.x;
-  const uint64_t back = a.tiles_per_chunk;  // tile (r-1, seg) is tile - tiles_per_chunk, modulo ntiles
-  const uint64_t w = holder_of(a, t >= back ? t - back : t + a.ntiles - back);
-  return w == blockIdx.x ? -1 : static_cast<int>(w);
+// The lane's flag: a workgroup index, or -1 for none (no such tiles, or
+// tiles whose upstream tiles are the workgroup's own, whose steps before
+// are done).
+__device__ inline int flags_upstream(const RingArgs& a) {
+  // Everything below is 32-bit arithmetic on offsets the host reduced
+  // modulo G: f < G, and every offset is below G.
+  const unsigned g = gridDim.x, f = static_cast<unsigned>(first_tile(a, blockIdx.x));
+  const auto slot_holder = [&](unsigned m) -> unsigned {  // the holder of tiles m (mod G), for m < 2G
+    m = m >= g ? m - g : m;
+    return a.xcd_map ? (m % (g / 8)) * 8 + m / (g / 8) : m;
+  };
+  const unsigned last_off = a.ntiles_mod + g - 1 - f;  // (ntiles - 1 - f) mod G, before the reduction
+  const uint64_t last = a.ntiles - 1 - (last_off >= g ? last_off - g : last_off);  // b's last tile
+  // The two candidates are the same in every lane.  Said so explicitly
+  // (readfirstlane), the compiler keeps them in scalar registers; left to
+  // its own analysis it held more of the kernel in vector registers and the
+  // 1024-lane float32 and bf16 forms spilled.
+  const unsigned back = __builtin_amdgcn_readfirstlane(last >= a.tiles_per_chunk  // some tile is not rank 0's
+                                                           ? slot_holder(f + a.up_back)
+                                                           : ~0u);
+  const unsigned wrap = __builtin_amdgcn_readfirstlane(f < a.tiles_per_chunk  // some tile is rank 0's
+                                                           ? slot_holder(f + a.up_wrap)
+                                                           : ~0u);
+  const int w = threadIdx.x == 0 ? int(back) : threadIdx.x == 1 ? int(wrap) : -1;
+  return w == int(blockIdx.x) ? -1 : w;
 }
 
 // A flag word holds the steps its workgroup has completed in its low 24
@@ -424,19 +435,18 @@ __device__ inline int flags_upstream(const RingArgs& a, bool whole_grid) {
 constexpr unsigned kFlagSteps = 0xFFFFFFu;
 __device__ inline unsigned xcd_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)); }
 
-// Waits until the flags reach `step`; false once the poll limit is reached
-// or another workgroup has raised the abort word.  `bad` is
-// workgroup-shared, 0 until a wait fails; the workgroup then stops.
-// `local` (workgroup-shared) gets bit i set when the i-th tile's upstream
-// workgroup runs on this workgroup's XCD (or is this workgroup), read from
-// the XCD field of the flag it waited on; never in the whole-grid form.
-__device__ inline bool flags_wait(const RingArgs& a, int step, int first, bool whole_grid, unsigned xcd, int* bad,
-                                  uint64_t* local) {
+// Waits until the flag of the lane's workgroup `w` reaches `step`; false
+// once the poll limit is reached or another workgroup has raised the abort
+// word.  `bad` is workgroup-shared, 0 until a wait fails; the workgroup then
+// stops.  `near` (workgroup-shared) gets bit 0 set when the workgroup
+// holding the upstream tiles of the tiles from T on runs on this
+// workgroup's XCD (or is this workgroup), and bit 1 for the tiles below T,
+// read from the XCD field of the flag waited on.
+__device__ inline bool flags_wait(const RingArgs& a, int step, int w, unsigned xcd, int* bad, unsigned* near) {
   if (threadIdx.x < 64) {
-    unsigned spins = 0;
-    bool ok = true, near = !whole_grid;
-    for (int w = first; ok && w >= 0 && w < int(gridDim.x); w = whole_grid ? w + 64 : -1) {
-      if (w == int(blockIdx.x)) continue;
+    bool ok = true, same = true;
+    if (w >= 0) {
+      unsigned spins = 0;
       const unsigned* flag = a.ctrl + kCtrlFlags + w;
       unsigned v;
       while (((v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & kFlagSteps) <
@@ -450,11 +460,11 @@ __device__ inline bool flags_wait(const RingArgs& a, int step, int first, bool w
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      near = near && (v >> 24) == xcd;
+      same = (v >> 24) == xcd;
     }
-    const uint64_t mask = __ballot(near);
+    const uint64_t mask = __ballot(same);
     if (!ok) *bad = 1;
-    if (threadIdx.x == 0) *local = mask;
+    if (threadIdx.x == 0) *near = unsigned(mask & 3u);
   }
   __syncthreads();
   return *bad == 0;
@@ -501,12 +511,11 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a
   using LA = Lane<T, P, true, true, false>;
   constexpr bool kAhead = CCL_SIM_FLAGS_AHEAD && sizeof(typename T::A) == sizeof(typename T::S);
   __shared__ int s_bad;
-  __shared__ uint64_t s_local;
+  __shared__ unsigned s_near;
   const int n = a.nranks;
   const int nsteps = (a.coll == kAllReduce) ? 2 * (n - 1) : (a.coll == kReduceScatter ? n - 1 : n);
   const unsigned xcd = xcd_id();
-  const bool whole_grid = tiles_of_block(a) > 64;
-  const int up = flags_upstream(a, whole_grid);
+  const int up = flags_upstream(a);
   const uint64_t t0 = first_tile(a, blockIdx.x);  // < ntiles: the grid is at most ntiles
   const int r0 = rank_of_tile(t0, a.tiles_per_chunk);
   const uint64_t seg0 = t0 - uint64_t(r0) * a.tiles_per_chunk;
@@ -515,7 +524,8 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a
   for (int step = a.first_step; step < nsteps; ++step) {
     bool have_ahead = false;
     RsTileAt first;
-    uint64_t local = a.xcd_loads ? ~uint64_t(0) : 0;
+    // Bit 0: the tiles from T on read from the L2; bit 1: the tiles below T.
+    unsigned local = a.xcd_loads ? 3u : 0u;
     if (step > a.first_step) {
       if (kAhead && a.coll != kAllGather && step < n - 1) {
         first = rs_tile_at<P, T>(a, step, r0, seg0);
@@ -533,15 +543,15 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a
           have_ahead = true;
         }
       }
-      if (!flags_wait(a, step, up, whole_grid, xcd, &s_bad, &s_local)) return;
-      local = a.xcd_loads ? s_local : 0;
+      if (!flags_wait(a, step, up, xcd, &s_bad, &s_near)) return;
+      local = a.xcd_loads ? __builtin_amdgcn_readfirstlane(s_near) : 0u;
       // Ordinary loads may hit this CU's L1, which can hold a line read at
       // an earlier step (in the in-place forms a step can read again what
       // the first step read).  Drop the L1 (this CU's own cache only)
       // before reading what the wait released from the L2.
       if (local != 0) asm volatile("buffer_inv sc0" ::: "memory");
     }
-    if (local & 1) {
+    if ((local >> (t0 < a.tiles_per_chunk ? 1 : 0)) & 1u) {
       if (have_ahead)
         ring_rs_tile<T, OP, P, true, true, true>(a, step, first.r, first.seg, first.c, first.len, ahead);
       else
@@ -552,9 +562,8 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_flags_kernel(RingArgs a
       else
         ring_body<T, OP, P, true, true, false>(a, step, 0, r0, seg0);
     }
-    int i = 1;
-    for (uint64_t tile = t0 + gridDim.x; tile < a.ntiles; tile += gridDim.x, ++i) {
-      if (i < 64 && ((local >> i) & 1))
+    for (uint64_t tile = t0 + gridDim.x; tile < a.ntiles; tile += gridDim.x) {
+      if ((local >> (tile < a.tiles_per_chunk ? 1 : 0)) & 1u)
         ring_body<T, OP, P, true, false, true>(a, step, tile);
       else
         ring_body<T, OP, P, true>(a, step, tile);
@@ -727,6 +736,9 @@ hipError_t launch_persistent(const Call& c, bool* unsupported, PersistentPlan* p
   // less than an eighth of the grid apart.
   a.xcd_map = FLAGS && grid % 8 == 0 && a.tiles_per_chunk % 8 != 0 && a.tiles_per_chunk < grid / 8 ? 1 : 0;
   a.xcd_loads = FLAGS && c.line_aligned ? 1 : 0;
+  a.up_back = static_cast<unsigned>((grid - a.tiles_per_chunk % grid) % grid);
+  a.up_wrap = static_cast<unsigned>((a.ntiles - a.tiles_per_chunk) % grid);
+  a.ntiles_mod = static_cast<unsigned>(a.ntiles % grid);
   if (plan) {
     plan->occupancy_per_cu = per_cu;
     plan->per_cu = use;

@@ -204,6 +204,39 @@ def test_large_steps_every_element(cs, sync):
     torch.cuda.empty_cache()
 
 
+LARGE_ALIGNED = [
+    # n, q, dtype, op.  256-lane tiles (4,096 float32 or 8,192 bf16 elements)
+    # at steps above 2^26 elements, 64 to 82 tiles per workgroup of the
+    # 256-workgroup grid, whose upstream tiles sit on two other workgroups.
+    (8, 4096 * 2100, "float32", "sum"),
+    (3, 4096 * 7000, "float32", "max"),
+    (8, 8192 * 2100, "bfloat16", "sum"),
+]
+
+
+@pytest.mark.parametrize("n,q,dtype,op", LARGE_ALIGNED)
+def test_large_line_aligned_steps_match_stepwise(cs, n, q, dtype, op):
+    """Forced step flags on large line-aligned steps, where each workgroup
+    holds many tiles per step and reads same-XCD data from the L2:
+    AllReduce and ReduceScatter, every element of every rank against the
+    stepwise ring."""
+    saved = os.environ.get("CCL_SIM_PERSISTENT_SYNC")
+    os.environ["CCL_SIM_PERSISTENT_SYNC"] = "flags"
+    try:
+        xs = U.random_inputs(n, n * q, dtype, seed=n * 7 + len(dtype), op=op)
+        for coll in ("allreduce", "reduce_scatter"):
+            got, want = run_pair(cs, coll, xs, dtype, op, False, q=q)
+            for r in range(n):
+                assert dev_equal(got[r], want[r], dtype), f"{coll} n={n} q={q} {dtype} rank {r}"
+            del got, want
+            torch.cuda.empty_cache()
+    finally:
+        if saved is None:
+            os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
+        else:
+            os.environ["CCL_SIM_PERSISTENT_SYNC"] = saved
+
+
 def test_unknown_value_is_refused_before_any_launch(cs):
     saved = os.environ.get("CCL_SIM_PERSISTENT_SYNC")
     os.environ["CCL_SIM_PERSISTENT_SYNC"] = "barrier"
