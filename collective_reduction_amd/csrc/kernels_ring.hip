@@ -376,8 +376,10 @@ __global__ __launch_bounds__(P::TB) void ring_persistent_kernel(RingArgs a) {
 //
 // Ordering, on the agent-coherent data path only: a workgroup's waves wait
 // for their stores (write-through) to complete before lane 0 publishes the
-// flag, and the loads of data written by other workgroups are agent-scope
-// (sc1) loads issued after the wait, so no cache maintenance is needed.
+// flag, and the loads of data written by other workgroups are issued after
+// the wait, as agent-scope (sc1) loads, or, where the writer runs on the
+// same XCD, as ordinary loads from that XCD's L2 once the CU's L1 has been
+// dropped (below).  No other cache maintenance is needed.
 //
 // Placement.  Workgroup b holds the tiles f(b), f(b) + G, f(b) + 2G, ...
 // (G = gridDim.x), where f is the identity, or, with xcd_map, the
