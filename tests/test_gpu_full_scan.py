@@ -176,3 +176,24 @@ def test_uniform_8x134217728_bf16_every_element(cs, schedule):
     w = workload("uniform_8x268435456_fp32", count=1 << 27, dtype="bfloat16")
     w.check_tolerance()
     w.run_and_compare(cs, schedule)
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_max_ranks_1024_fp32_every_element(cs, schedule):
+    """The largest rank count the library accepts, 1,024 ranks of 320
+    float32 elements (whole 128-byte lines, so the persistent ring's step
+    flags read same-XCD data from the L2, with the XCD placement of its
+    workgroups): 2,046 ring steps, pointer tables in the workspace, ten
+    halving levels, every tile ragged."""
+    w = workload("normal_256x4194304_fp32", nranks=1024, count=1024 * 320)
+    w.check_tolerance()
+    w.run_and_compare(cs, schedule)
+
+
+@pytest.mark.parametrize("schedule", U.SCHEDULES)
+def test_max_ranks_1024_int32_every_element(cs, schedule):
+    """1,024 ranks of 301 int32 elements (chunks off the line grid):
+    integer SUM is exact in any order, so every schedule must reproduce the
+    same values at every position."""
+    w = workload("intuniform_8x1000003_int32", nranks=1024, count=1024 * 301)
+    w.run_and_compare(cs, schedule)
