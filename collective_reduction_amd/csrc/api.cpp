@@ -392,11 +392,11 @@ ccl_sim_result_t run_collective(int coll, const void* const* sendbufs, void* con
     if (c.log_plan)
       std::fprintf(stderr,
                    "[ccl_sim] persistent coll=%d N=%d q=%llu cus=%d occupancy/cu=%d used/cu=%d grid=%llu lanes=%d "
-                   "tiles/step=%llu coherent=%d sync=%s\n",
+                   "tiles/step=%llu coherent=%d sync=%s same_xcd_reads=%d\n",
                    coll, nranks, static_cast<unsigned long long>(q), c.num_cus, plan.occupancy_per_cu, plan.per_cu,
                    static_cast<unsigned long long>(plan.grid), plan.lanes,
                    static_cast<unsigned long long>(plan.tiles_per_step), plan.coherent ? 1 : 0,
-                   plan.flags ? "flags" : "grid");
+                   plan.flags ? "flags" : "grid", plan.flags && c.line_aligned ? 1 : 0);
     if (e == hipSuccess && c.log_plan) {
       // Debug check of the watchdog: wait for the kernel and read the abort
       // word it raises when a barrier or flag wait runs into the poll limit.

@@ -237,6 +237,36 @@ def test_large_line_aligned_steps_match_stepwise(cs, n, q, dtype, op):
             os.environ["CCL_SIM_PERSISTENT_SYNC"] = saved
 
 
+def test_debug_plan_names_the_same_xcd_reads(cs, capfd):
+    """The launch plan that CCL_SIM_DEBUG=1 prints says whether a
+    flag-ordered call reads same-XCD data from the L2: on when every chunk
+    and rank buffer is made of whole 128-byte lines, off when a chunk ends
+    inside a line."""
+    saved = {k: os.environ.get(k) for k in ("CCL_SIM_DEBUG", "CCL_SIM_PERSISTENT_SYNC")}
+    os.environ["CCL_SIM_DEBUG"] = "1"
+    os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
+    try:
+        n = 8
+        for q, want in ((1024, 1), (1001, 0)):
+            m = n * q
+            send = [torch.rand(m, device="cuda") for _ in range(n)]
+            recv = [torch.empty(m, device="cuda") for _ in range(n)]
+            ws = cs.Workspace("allreduce", n, m, "float32", "ring_persistent")
+            capfd.readouterr()
+            cs.ccl_sim_allreduce(send, recv, m, schedule="ring_persistent", workspace=ws)
+            torch.cuda.synchronize()
+            lines = [ln for ln in capfd.readouterr().err.splitlines() if ln.startswith("[ccl_sim] persistent")]
+            assert lines, "no launch plan printed"
+            assert "sync=flags" in lines[-1] and f"same_xcd_reads={want}" in lines[-1], lines[-1]
+            assert torch.allclose(recv[0], torch.stack(send).sum(0), rtol=0, atol=1e-5 * n)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 def test_unknown_value_is_refused_before_any_launch(cs):
     saved = os.environ.get("CCL_SIM_PERSISTENT_SYNC")
     os.environ["CCL_SIM_PERSISTENT_SYNC"] = "barrier"
