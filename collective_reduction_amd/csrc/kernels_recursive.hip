@@ -42,6 +42,71 @@ struct RecArgs {
   void* scratch;
 };
 
+// bf16 partials (eight float32 accumulators, 32 bytes, per lane) in the
+// stepwise driver's natural layout.  Moved lane by lane, each of a wave's
+// two 16-byte accesses covers every other 16 bytes of 2 KB, half of every
+// line it touches.  Whole tiles instead move a wave's 2 KB as two
+// contiguous 1 KB halves, lane i taking bytes [16i, 16i + 16) of each, and
+// the lanes trade values through the cross-lane permute (ds_bpermute,
+// which reads another lane's register without touching LDS memory), so
+// that each lane still folds its own eight positions.  The layout in
+// memory stays the natural one, which the stepwise driver needs: it tiles
+// each halving step afresh.  Every lane of the wave takes part, which whole
+// tiles guarantee.
+#ifndef CCL_SIM_RECURSIVE_WAVE_ACC
+#define CCL_SIM_RECURSIVE_WAVE_ACC 1
+#endif
+__device__ inline float lane_value(int src_lane, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
+}
+
+// The wave's 512 positions from `wave_base` (its first lane's first
+// position); returns this lane's eight accumulators.
+template <class P, class AV>
+__device__ inline AV wave_load_acc8(const float* wave_base) {
+  static_assert(sizeof(AV) == 32, "eight float32 accumulators");
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const auto a = vload<float, 4, P::NTL>(wave_base + 4 * lane);        // positions [4i, 4i + 4)
+  const auto b = vload<float, 4, P::NTL>(wave_base + 256 + 4 * lane);  // positions [256 + 4i, 256 + 4i + 4)
+  // lane j holds positions [8j, 8j + 8): the first half in lane 2j's and the
+  // second in lane 2j + 1's access (of a for j < 32, of b above)
+  const int s0 = 2 * (lane & 31), s1 = s0 + 1;
+  const bool upper = lane >= 32;
+  AV v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a0 = lane_value(s0, a[k]), b0 = lane_value(s0, b[k]);
+    const float a1 = lane_value(s1, a[k]), b1 = lane_value(s1, b[k]);
+    v[k] = upper ? b0 : a0;
+    v[4 + k] = upper ? b1 : a1;
+  }
+  return v;
+}
+
+// Stores this lane's eight accumulators as the wave's 2 KB from the byte
+// offset `wave_off` of the tile that starts at `tile_base` (`tile_bytes`
+// long), with write-through stores of whole lines.
+template <class AV>
+__device__ inline void wave_store_acc8(float* tile_base, uint32_t tile_bytes, uint32_t wave_off, AV v) {
+  static_assert(sizeof(AV) == 32, "eight float32 accumulators");
+  using F4 = typename VecOf<float, 4>::type;
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  // access a, lane i: positions [4i, 4i + 4), the first or second half of
+  // lane i/2's eight; access b: the same of lane 32 + i/2
+  const int src = lane >> 1;
+  const bool second = lane & 1;
+  F4 a, b;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = lane_value(src, v[k]), x1 = lane_value(src, v[4 + k]);
+    const float y0 = lane_value(32 + src, v[k]), y1 = lane_value(32 + src, v[4 + k]);
+    a[k] = second ? x1 : x0;
+    b[k] = second ? y1 : y0;
+  }
+  store_through(tile_base, tile_bytes, wave_off + uint32_t(16 * lane), a);
+  store_through(tile_base, tile_bytes, wave_off + 1024u + uint32_t(16 * lane), b);
+}
+
 // Halving step `step` for rank i over the tile `seg` of the range that
 // starts at position `base` (cnt valid positions from base).  SAME_TILING:
 // every step that touches these partials uses this same tile geometry (the
@@ -53,6 +118,9 @@ __device__ inline void halving_tile(const RecArgs& a, int step, bool last, int i
   using A = typename T::A;
   using L = Lane<T, P, FULL>;
   constexpr int V = vec_elems<T>();
+  // the wave-wide accesses above: natural-layout bf16 partials of a whole tile
+  constexpr bool kWave = CCL_SIM_RECURSIVE_WAVE_ACC && !SAME_TILING && FULL && sizeof(typename L::AV) == 32 &&
+                         P::ST == kStoreWriteThrough && P::TB % 64 == 0;
   const int n = a.nranks;
   const int d = n >> step;
   const int p = i ^ d;
@@ -84,6 +152,10 @@ __device__ inline void halving_tile(const RecArgs& a, int step, bool last, int i
         if constexpr (SAME_TILING) {
           vl[u] = ln.load_part(wl, u);
           vu[u] = ln.load_part(wu, u);
+        } else if constexpr (kWave) {
+          const uint64_t first = ln.j[u] - uint64_t(static_cast<int>(threadIdx.x) & 63) * V;  // the wave's first position
+          vl[u] = wave_load_acc8<P, typename L::AV>(wl + first);
+          vu[u] = wave_load_acc8<P, typename L::AV>(wu + first);
         } else {
           vl[u] = ln.load_acc(wl, u);
           vu[u] = ln.load_acc(wu, u);
@@ -98,10 +170,15 @@ __device__ inline void halving_tile(const RecArgs& a, int step, bool last, int i
       typename L::AV v;
 #pragma unroll
       for (int k = 0; k < V; ++k) v[k] = combine<T, OP>(vl[u][k], vu[u][k]);
-      if constexpr (SAME_TILING)
+      if constexpr (SAME_TILING) {
         ln.store_part(dst, u, v);
-      else
+      } else if constexpr (kWave) {
+        const uint32_t wave_off =
+            uint32_t((u * P::TB + (static_cast<int>(threadIdx.x) & ~63)) * V * int(sizeof(A)));
+        wave_store_acc8(dst + ln.t0, uint32_t(tile_of<P>(V) * sizeof(A)), wave_off, v);
+      } else {
         ln.store_acc(dst, u, v);
+      }
     }
   } else {
     typename T::S* dst = (a.coll == kAllReduce) ? out_ptr<T>(a.recv, i) + base : out_ptr<T>(a.recv, i);
