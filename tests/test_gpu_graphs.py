@@ -7,7 +7,6 @@ captures one call, then replays the graph several times with new inputs
 written by eager work between the replays, and checks every replay bit for
 bit against an eager call of the same collective on the same inputs."""
 
-import numpy as np
 import pytest
 import torch
 
