@@ -247,6 +247,8 @@ def test_debug_plan_names_the_same_xcd_reads(cs, capfd):
     os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
     try:
         n = 8
+        # separate torch allocations start on 512-byte boundaries, so the
+        # rank buffers are line-aligned and q alone decides
         for q, want in ((1024, 1), (1001, 0)):
             m = n * q
             send = [torch.rand(m, device="cuda") for _ in range(n)]
