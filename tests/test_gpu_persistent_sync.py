@@ -238,10 +238,11 @@ def test_large_line_aligned_steps_match_stepwise(cs, n, q, dtype, op):
 
 
 def test_debug_plan_names_the_same_xcd_reads(cs, capfd):
-    """The launch plan that CCL_SIM_DEBUG=1 prints says whether a
+    """The launch plan that CCL_SIM_DEBUG=1 prints names the step ordering
+    that ccl_sim_persistent_ordering predicts, and says whether a
     flag-ordered call reads same-XCD data from the L2: on when every chunk
     and rank buffer is made of whole 128-byte lines, off when a chunk ends
-    inside a line."""
+    inside a line (and always off under the grid barrier)."""
     saved = {k: os.environ.get(k) for k in ("CCL_SIM_DEBUG", "CCL_SIM_PERSISTENT_SYNC")}
     os.environ["CCL_SIM_DEBUG"] = "1"
     os.environ.pop("CCL_SIM_PERSISTENT_SYNC", None)
@@ -249,8 +250,11 @@ def test_debug_plan_names_the_same_xcd_reads(cs, capfd):
         n = 8
         # separate torch allocations start on 512-byte boundaries, so the
         # rank buffers are line-aligned and q alone decides
-        for q, want in ((1024, 1), (1001, 0)):
+        # (q, ordering, same-XCD reads); q = 2^24 makes a step of 2^27
+        # elements, above the flags' default range
+        for q, sync, want in ((1024, "flags", 1), (1001, "flags", 0), (1 << 24, "grid", 0)):
             m = n * q
+            assert cs.ccl_sim_persistent_ordering("allreduce", n, m) == sync
             send = [torch.rand(m, device="cuda") for _ in range(n)]
             recv = [torch.empty(m, device="cuda") for _ in range(n)]
             ws = cs.Workspace("allreduce", n, m, "float32", "ring_persistent")
@@ -259,8 +263,10 @@ def test_debug_plan_names_the_same_xcd_reads(cs, capfd):
             torch.cuda.synchronize()
             lines = [ln for ln in capfd.readouterr().err.splitlines() if ln.startswith("[ccl_sim] persistent")]
             assert lines, "no launch plan printed"
-            assert "sync=flags" in lines[-1] and f"same_xcd_reads={want}" in lines[-1], lines[-1]
+            assert f"sync={sync}" in lines[-1] and f"same_xcd_reads={want}" in lines[-1], lines[-1]
             assert torch.allclose(recv[0], torch.stack(send).sum(0), rtol=0, atol=1e-5 * n)
+            del send, recv, ws
+        torch.cuda.empty_cache()
     finally:
         for k, v in saved.items():
             if v is None:
